@@ -1,0 +1,180 @@
+"""Benchmark: grouped blockwise-FP8 MoE GEMM on one MI355X.
+
+One step = one pass of the hot path over one batch of the large MoE workload (32 local
+experts, 16384 tokens at top-8 = 131072 expert rows, Dirichlet(1.0) routing with two empty
+experts, padded to 128-row tiles):
+    1. token-to-expert tile map from the per-expert counts (GPU kernel),
+    2. gate_up grouped GEMM  N=4096, K=7168  (e4m3, 1x128 / 128x128 fp32 scales, bf16 out),
+    3. down    grouped GEMM  N=7168, K=2048  (same formats).
+Inputs are synthetic (seeded) and resident in HBM before the timed region. ``value`` is
+useful TFLOP/s (2 * real rows * N * K summed over both GEMMs, padding rows excluded) per
+step time. The JSON line also carries the roofline of the dominant kernel (gate_up), whose
+per-launch time is measured with HIP events on the stream the kernels run on, and the CPU
+oracle's rate on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5033.0   # MI355X dense FP8 MFMA peak (256 CU x 2.4 GHz x 8192 flop/clk)
+PEAK_HBM_GBS = 8000.0
+METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(problems, n_experts=8, rows_per_expert=64):
+    """Time the oracle on a bounded sample: ``rows_per_expert`` real rows of each of the first
+    ``n_experts`` non-empty experts of the gate_up GEMM. Returns the JSON object."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as og
+    from workloads.generate import padded_starts
+
+    p = problems["gate_up"]
+    starts = padded_starts(p.counts)
+    experts = [e for e in range(p.E) if p.counts[e] > 0][:n_experts]
+    work, flops = [], 0.0
+    for e in experts:
+        r = min(rows_per_expert, int(p.counts[e]))
+        s = int(starts[e])
+        work.append((p.qa[s:s + r].cpu().numpy(), p.a_scales[s:s + r].cpu().numpy(),
+                     p.qb[e].cpu().numpy(), p.b_scales[e].cpu().numpy()))
+        flops += 2.0 * r * p.N * p.K
+    t0 = time.perf_counter()
+    for qa, sa, qb, sb in work:
+        og.blockwise_grouped(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"gate_up GEMM, {rows_per_expert} real rows of each of {len(experts)} experts "
+                  f"(N={p.N}, K={p.K}), fp64 oracle K block by K block; {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(each GPU would run its own experts' share; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mx_grouped_gemm_amd as bsg
+    from workloads.generate import make_problem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    bsg.load_library()
+
+    problems = {
+        "gate_up": make_problem("moe32_gate_up_n4096_k7168", device="cuda", seed=args.seed),
+        "down": make_problem("moe32_down_n7168_k2048", device="cuda", seed=args.seed),
+    }
+    gu, dn = problems["gate_up"], problems["down"]
+    assert np.array_equal(gu.counts, dn.counts)
+    counts = torch.tensor(gu.counts, dtype=torch.int32, device=dev)
+    T = gu.M // 128
+    expert_offsets = torch.empty(gu.E + 1, dtype=torch.int32, device=dev)
+    tile_offsets = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(T, dtype=torch.int32, device=dev)
+    C_gu = torch.empty(gu.M, gu.N, dtype=torch.bfloat16, device=dev)
+    C_dn = torch.empty(dn.M, dn.N, dtype=torch.bfloat16, device=dev)
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
+    stream = torch.cuda.current_stream()
+
+    names = ("tile_map", "gate_up", "down")
+    ev = {n: [] for n in names}
+
+    def step(record):
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        a = mark() if record else None
+        bsg.bsgemm_build_tiles(counts, T, True, expert_offsets, tile_offsets, expert_ids, stream)
+        b = mark() if record else None
+        bsg.bsgemm_grouped(gu.qa, gu.a_scales, gu.qb, gu.b_scales, expert_ids, tile_offsets, C_gu,
+                           gu.M, gu.N, gu.K, fmt, num_tiles=T, num_experts=gu.E, stream=stream)
+        c = mark() if record else None
+        bsg.bsgemm_grouped(dn.qa, dn.a_scales, dn.qb, dn.b_scales, expert_ids, tile_offsets, C_dn,
+                           dn.M, dn.N, dn.K, fmt, num_tiles=T, num_experts=dn.E, stream=stream)
+        d = mark() if record else None
+        if record:
+            ev["tile_map"].append((a, b))
+            ev["gate_up"].append((b, c))
+            ev["down"].append((c, d))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    kernel_ms = {n: float(np.mean([s.elapsed_time(e) for s, e in ev[n]])) for n in names}
+    useful = {n: p.useful_flops for n, p in problems.items()}
+    total_flops = useful["gate_up"] + useful["down"]
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    gu_tflops = useful["gate_up"] / (kernel_ms["gate_up"] * 1e-3) / 1e12
+    dn_tflops = useful["down"] / (kernel_ms["down"] * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe32_16384tok_top8: tile map + gate_up (N=4096, K=7168) + down "
+                        "(N=7168, K=2048), blockwise e4m3 1x128/128x128 fp32 scales, bf16 out",
+            "experts": gu.E, "tokens": 16384, "top_k": 8, "real_rows": gu.real_rows,
+            "padded_rows": gu.M, "m_tiles": T, "seed": args.seed,
+        },
+        "kernels_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
+        "kernels_tflops": {"gate_up": round(gu_tflops, 1), "down": round(dn_tflops, 1)},
+        "roofline": {
+            "kernel": "bw_fp8_grouped_kernel (gate_up launch)",
+            "bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(problems)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * bsgemm.h - C ABI of the MI355X (gfx950) grouped block-scaled low-precision GEMM.
+ *
+ * The operation is the grouped, blockwise-FP8 MoE matmul whose per-K-block promote step is
+ * described on the Modular MAX page "promote_accumulators"
+ * (kernels/linalg/grouped_matmul_sm100_blockwise_fp8; description paragraph and section
+ * Args), with the per-K-iteration cadence of the Modular MAX page "EpilogueWarpContext"
+ * (method per_k_stage), plus the MX variant of the Triton Gluon page "Overlapping
+ * Accumulator Block-Scaled Matrix Multiplication" (e8m0 scale per 32 K-elements, applied
+ * inside the matrix instruction; reference result A_ref @ B_ref^T in its make_problem).
+ *
+ * General rules for every entry point:
+ *  - Pointers marked DEVICE are device (HBM) pointers owned by the caller. The library
+ *    never allocates, frees or retains them. Pointers marked HOST are host pointers.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL means
+ *    the null stream) on the current HIP device. Calls return after enqueueing.
+ *  - Return value: BSG_OK (0) or a negative bsg_status. Arguments are validated on the host
+ *    before anything is enqueued; on any error nothing is enqueued and outputs are untouched.
+ *  - Thread-safe: no global mutable state apart from a per-device property cache.
+ *  - Device-side contents (tile map, counts) cannot be checked on the host. The kernels clamp
+ *    them instead: a tile whose expert id is outside [0, num_experts) is skipped, rows are
+ *    clamped into [0, M), and negative counts count as zero. Such input gives unspecified
+ *    (but in-bounds) results.
+ */
+#ifndef BSGEMM_H
+#define BSGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSG_OK = 0,
+  BSG_ERR_NULL = -1,    /* a required pointer is NULL                                   */
+  BSG_ERR_SHAPE = -2,   /* a size is negative, too large, or not a multiple it must be  */
+  BSG_ERR_ALIGN = -3,   /* a pointer is not aligned as documented                      */
+  BSG_ERR_FMT = -4,     /* unsupported fmt combination                                 */
+  BSG_ERR_DEVICE = -5,  /* no HIP device, or the current device is not gfx950          */
+  BSG_ERR_LAUNCH = -6   /* the HIP runtime rejected a kernel launch                    */
+} bsg_status;
+
+/* ---- fmt: element formats, scale kind and output type, packed into one word ------------ */
+#define BSG_ELEM_E4M3 1u   /* OCP e4m3fn, one byte per element                            */
+#define BSG_ELEM_E2M1 2u   /* OCP e2m1, two per byte along K, even K index in low nibble  */
+#define BSG_SCALE_BLOCKWISE 1u /* fp32: A per row per 128 K; B per 128 (N) x 128 (K) block */
+#define BSG_SCALE_MX 2u        /* e8m0 (uint8, 2^(x-127)): one per row per 32 K, A and B   */
+#define BSG_OUT_F32 1u
+#define BSG_OUT_BF16 2u
+#define BSG_OUT_F16 3u
+#define BSG_FMT(a_elem, b_elem, scale, out) \
+  ((uint32_t)(a_elem) | ((uint32_t)(b_elem) << 4) | ((uint32_t)(scale) << 8) | ((uint32_t)(out) << 12))
+
+/*
+ * bsgemm_build_tiles - token-to-expert tile map (the scheduler build).
+ *
+ * Passage: "promote_accumulators", section Args, argument expert_ids (maps a group of rows
+ * to its expert in B) and argument scheduler (tracks the current group and work tile).
+ *
+ * Rows of A are grouped by expert in ascending expert order. From the per-expert row counts
+ * this writes, with T = num_tiles:
+ *   expert_offsets[e]  first row of expert e's group; expert_offsets[E] = rows the layout needs
+ *   tile_offsets[t]    first row of M-tile t (t in [0, T]); tile t owns
+ *                      min(128, max(0, tile_offsets[t+1] - tile_offsets[t])) rows
+ *   expert_ids[t]      expert of M-tile t, or -1 for tiles past the last expert's rows
+ * padded != 0: each group starts at a multiple of 128 rows, tile_offsets[t] = 128 t, and tiles
+ *   include the group's padding rows.
+ * padded == 0: groups are packed back to back; each group's last tile is ragged; tiles past
+ *   the last one start at expert_offsets[E].
+ * If the layout needs more than T tiles, the extra tiles are dropped (expert_offsets[E] still
+ * reports the rows needed, so the caller can detect it).
+ *
+ *   counts          DEVICE int32[num_experts], row count per expert (>= 0)
+ *   num_experts     1 .. 4096
+ *   num_tiles       >= 0
+ *   expert_offsets  DEVICE int32[num_experts + 1] (output)
+ *   tile_offsets    DEVICE int32[num_tiles + 1]   (output)
+ *   expert_ids      DEVICE int32[num_tiles]       (output; may be NULL iff num_tiles == 0)
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN (int32 alignment), BSG_ERR_DEVICE,
+ * BSG_ERR_LAUNCH.
+ */
+int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_tiles,
+                       int32_t padded, int32_t* expert_offsets, int32_t* tile_offsets,
+                       int32_t* expert_ids, void* stream);
+
+/*
+ * bsgemm_grouped - grouped block-scaled GEMM  C[rows of tile t] = A[rows] * B[e]^T, e = expert_ids[t].
+ *
+ * Blockwise (scale kind BSG_SCALE_BLOCKWISE; passage: "promote_accumulators", description
+ * paragraph, and Args b_scales / b_scales_n / k_iter / expert_ids / problem_shape):
+ *   for every K block kb of 128:  P = sum_{k in kb} qa[m,k] * qb[e,n,k]   (fp32, fresh each block)
+ *                                 acc[m,n] += P * (a_scales[m,kb] * b_scales[e, n/128, kb])
+ *   C[m,n] = acc[m,n] converted to the output type (round to nearest even).
+ * MX (BSG_SCALE_MX; passage: Gluon page, random_quantized_tensor / async_mma_scaled_impl):
+ *   C[m,n] = sum_k (qa[m,k] 2^(sa[m,k/32]-127)) (qb[e,n,k] 2^(sb[e,n,k/32]-127)), scales
+ *   applied by the gfx950 scaled matrix instruction, fp32 accumulation.
+ *
+ * Layouts (all row-major, contiguous):
+ *   A          DEVICE [M, K] e4m3 bytes, or [M, K/2] packed e2m1. 16-byte aligned.
+ *   a_scales   blockwise: DEVICE float[M, K/128];  MX: DEVICE uint8[M, K/32]. 4-byte aligned.
+ *   B          DEVICE [num_experts, N, K] e4m3 (or [num_experts, N, K/2] e2m1): K contiguous,
+ *              i.e. each expert's B is stored N-major ("NT" GEMM). 16-byte aligned.
+ *   b_scales   blockwise: DEVICE float[num_experts, N/128, K/128];
+ *              MX: DEVICE uint8[num_experts, N, K/32]. 4-byte aligned.
+ *   expert_ids DEVICE int32[num_tiles] and tile_offsets DEVICE int32[num_tiles + 1], as written
+ *              by bsgemm_build_tiles (either layout). Both NULL: one dense group, expert 0,
+ *              tiles of 128 rows, num_tiles ignored (M need not be a multiple of 128).
+ *   C          DEVICE [M, N] float / bf16 / fp16. 16-byte aligned. Rows of skipped tiles and
+ *              rows no tile covers are not written.
+ * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0, both multiples of 128; num_experts >= 1;
+ *   num_tiles >= 0.
+ * Supported fmt: blockwise with A = B = e4m3, any output type; MX with A, B in {e4m3, e2m1},
+ *   any output type.
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN, BSG_ERR_FMT, BSG_ERR_DEVICE,
+ *   BSG_ERR_LAUNCH.
+ */
+int bsgemm_grouped(const void* A, const void* a_scales, const void* B, const void* b_scales,
+                   const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles,
+                   void* C, int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                   void* stream);
+
+/* Static, human-readable text for a bsg_status value (never NULL). */
+const char* bsgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGEMM_H */

@@ -1,0 +1,132 @@
+"""MI355X-native grouped block-scaled low-precision GEMM.
+
+Python binding of ``libbsgemm.so`` (the C ABI declared in ``include/bsgemm.h``). It only
+marshals arguments: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream. There is no fallback: if the
+library is missing or the device is not gfx950 the calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BsgemmError", "ELEM", "SCALE", "OUT", "make_fmt", "bsgemm_build_tiles", "bsgemm_grouped",
+    "bsgemm_status_string", "library_path", "load_library",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libbsgemm.so")
+_lib = None
+
+ELEM = {"e4m3": 1, "e2m1": 2}
+SCALE = {"blockwise": 1, "mx": 2}
+OUT = {"f32": 1, "bf16": 2, "f16": 3}
+OUT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+EXPORTED = ("bsgemm_build_tiles", "bsgemm_grouped", "bsgemm_status_string")
+
+
+class BsgemmError(RuntimeError):
+    def __init__(self, func, status):
+        super().__init__(f"{func} failed: {bsgemm_status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libbsgemm.so`` and declare its C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m mx_grouped_gemm_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
+    lib.bsgemm_build_tiles.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.bsgemm_build_tiles.restype = ctypes.c_int
+    lib.bsgemm_grouped.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, u32, vp]
+    lib.bsgemm_grouped.restype = ctypes.c_int
+    lib.bsgemm_status_string.argtypes = [ctypes.c_int]
+    lib.bsgemm_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def bsgemm_status_string(status):
+    return load_library().bsgemm_status_string(int(status)).decode()
+
+
+def make_fmt(a_elem, b_elem, scale, out):
+    """Pack element formats, scale kind and output type into the C ABI's ``fmt`` word."""
+    return ELEM[a_elem] | (ELEM[b_elem] << 4) | (SCALE[scale] << 8) | (OUT[out] << 12)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def bsgemm_build_tiles(counts, num_tiles, padded=True, expert_offsets=None, tile_offsets=None,
+                       expert_ids=None, stream=None):
+    """Token-to-expert tile map from per-expert row counts (int32 device tensor).
+
+    Returns ``(expert_offsets[E+1], tile_offsets[T+1], expert_ids[T])`` int32 device tensors,
+    allocated here unless given.
+    """
+    _dev(counts, "counts", torch.int32)
+    E, dev = counts.numel(), counts.device
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if tile_offsets is None:
+        tile_offsets = torch.empty(num_tiles + 1, dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(max(num_tiles, 1), dtype=torch.int32, device=dev)
+    for t, n in ((expert_offsets, "expert_offsets"), (tile_offsets, "tile_offsets"), (expert_ids, "expert_ids")):
+        _dev(t, n, torch.int32)
+    st = load_library().bsgemm_build_tiles(_ptr(counts), E, int(num_tiles), 1 if padded else 0,
+                                           _ptr(expert_offsets), _ptr(tile_offsets),
+                                           _ptr(expert_ids), _stream(stream))
+    if st != 0:
+        raise BsgemmError("bsgemm_build_tiles", st)
+    return expert_offsets, tile_offsets, expert_ids[:num_tiles]
+
+
+def bsgemm_grouped(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, K, fmt,
+                   num_tiles=None, num_experts=None, stream=None):
+    """Grouped block-scaled GEMM into ``C`` (see ``include/bsgemm.h``).
+
+    ``expert_ids`` / ``tile_offsets`` may both be None (one dense group). ``num_tiles``
+    defaults to ``expert_ids.numel()``, ``num_experts`` to ``B.shape[0]`` for 3-D ``B``.
+    """
+    for t, n in ((A, "A"), (a_scales, "a_scales"), (B, "B"), (b_scales, "b_scales"), (C, "C")):
+        _dev(t, n)
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(tile_offsets, "tile_offsets", torch.int32)
+    if num_tiles is None:
+        num_tiles = expert_ids.numel() if expert_ids is not None else 0
+    if num_experts is None:
+        num_experts = B.shape[0] if B.dim() == 3 else 1
+    st = load_library().bsgemm_grouped(
+        _ptr(A), _ptr(a_scales), _ptr(B), _ptr(b_scales), _ptr(expert_ids), _ptr(tile_offsets),
+        int(num_tiles), _ptr(C), int(M), int(N), int(K), int(num_experts), int(fmt), _stream(stream))
+    if st != 0:
+        raise BsgemmError("bsgemm_grouped", st)
+    return C

@@ -1,0 +1,117 @@
+// C ABI of the grouped block-scaled GEMM library: argument validation, device check and
+// dispatch to the gfx950 kernels. Declarations and contracts: include/bsgemm.h.
+#include "../../include/bsgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per-device cache: 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return BSG_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return BSG_ERR_DEVICE;
+  int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return BSG_ERR_DEVICE;
+    }
+    known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(known, std::memory_order_relaxed);
+  }
+  return known == 1 ? BSG_OK : BSG_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" const char* bsgemm_status_string(int status) {
+  switch (status) {
+    case BSG_OK: return "ok";
+    case BSG_ERR_NULL: return "a required pointer is NULL";
+    case BSG_ERR_SHAPE: return "invalid size (negative, too large, or not a required multiple)";
+    case BSG_ERR_ALIGN: return "pointer not aligned as required";
+    case BSG_ERR_FMT: return "unsupported fmt combination";
+    case BSG_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case BSG_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_tiles,
+                                  int32_t padded, int32_t* expert_offsets, int32_t* tile_offsets,
+                                  int32_t* expert_ids, void* stream) {
+  if (num_experts < 1 || num_experts > 4096 || num_tiles < 0 || num_tiles == INT32_MAX)
+    return BSG_ERR_SHAPE;
+  if (!counts || !expert_offsets || !tile_offsets || (num_tiles > 0 && !expert_ids))
+    return BSG_ERR_NULL;
+  if (!aligned(counts, 4) || !aligned(expert_offsets, 4) || !aligned(tile_offsets, 4) ||
+      (expert_ids && !aligned(expert_ids, 4)))
+    return BSG_ERR_ALIGN;
+  if (int st = check_device()) return st;
+  hipError_t err = bsg::launch_build_tiles(counts, num_experts, num_tiles, padded ? 1 : 0,
+                                           expert_offsets, tile_offsets, expert_ids,
+                                           static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
+}
+
+extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B,
+                              const void* b_scales, const int32_t* expert_ids,
+                              const int32_t* tile_offsets, int32_t num_tiles, void* C, int32_t M,
+                              int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                              void* stream) {
+  const unsigned fa = fmt & 0xF, fb = (fmt >> 4) & 0xF, sk = (fmt >> 8) & 0xF, out = (fmt >> 12) & 0xF;
+  if ((fmt >> 16) != 0 || out < BSG_OUT_F32 || out > BSG_OUT_F16) return BSG_ERR_FMT;
+  if (sk == BSG_SCALE_BLOCKWISE) {
+    if (fa != BSG_ELEM_E4M3 || fb != BSG_ELEM_E4M3) return BSG_ERR_FMT;
+  } else if (sk == BSG_SCALE_MX) {
+    if ((fa != BSG_ELEM_E4M3 && fa != BSG_ELEM_E2M1) || (fb != BSG_ELEM_E4M3 && fb != BSG_ELEM_E2M1))
+      return BSG_ERR_FMT;
+  } else {
+    return BSG_ERR_FMT;
+  }
+  if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || num_experts < 1 || num_tiles < 0)
+    return BSG_ERR_SHAPE;
+  const bool dense = expert_ids == nullptr && tile_offsets == nullptr;
+  if (!dense && (expert_ids == nullptr || tile_offsets == nullptr)) return BSG_ERR_NULL;
+  if (!A || !a_scales || !B || !b_scales || !C) return BSG_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || (!dense && (!aligned(expert_ids, 4) || !aligned(tile_offsets, 4))))
+    return BSG_ERR_ALIGN;
+  if (M == 0 || (!dense && num_tiles == 0)) return BSG_OK;
+  if (int st = check_device()) return st;
+
+  bsg::GemmArgs args;
+  args.A = A;
+  args.a_scales = a_scales;
+  args.B = B;
+  args.b_scales = b_scales;
+  args.expert_ids = dense ? nullptr : expert_ids;
+  args.tile_offsets = dense ? nullptr : tile_offsets;
+  args.C = C;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.num_experts = dense ? 1 : num_experts;
+  args.num_tiles = dense ? (M + 127) / 128 : num_tiles;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = sk == BSG_SCALE_BLOCKWISE
+                       ? bsg::launch_blockwise_fp8(args, static_cast<int>(out), s)
+                       : bsg::launch_mx(args, static_cast<int>(fa), static_cast<int>(fb),
+                                        static_cast<int>(out), s);
+  return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
+}

@@ -1,0 +1,116 @@
+// Device helpers shared by the gfx950 kernels of the grouped block-scaled GEMM.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWave = 64;
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (which would also wait for
+// every outstanding prefetch). Callers wait for exactly the loads they need first.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS copies. The LDS destination is wave-uniform; lane i's bytes land at
+// lds + i * size (global_load_lds_dword / _dwordx4).
+__device__ __forceinline__ void g2lds16(const void* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ lds_void* as_lds(uint8_t* p) { return (lds_void*)p; }
+
+__device__ __forceinline__ v4i lds_read16(const uint8_t* p) { return *(const v4i*)p; }
+
+__device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS tile row. With 128-byte rows (8 chunks), chunk c
+// of local row r is stored at slot c ^ swz8(r); 16 consecutive rows read at the same chunk
+// then touch 16 different 16-byte bank groups. With 64-byte rows (4 chunks) the same holds
+// for swz4.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
+
+// Output conversions (round to nearest even).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+enum OutKind { kOutF32 = 1, kOutBF16 = 2, kOutF16 = 3 };
+
+// Store 4 consecutive fp32 values to C (row-major) at element offset `off` (a multiple of 4).
+template <int OUT>
+__device__ __forceinline__ void store4(void* C, size_t off, float a, float b, float c, float d) {
+  if constexpr (OUT == kOutF32) {
+    *(v4i*)((float*)C + off) = (v4i){(int)__float_as_uint(a), (int)__float_as_uint(b),
+                                     (int)__float_as_uint(c), (int)__float_as_uint(d)};
+  } else if constexpr (OUT == kOutBF16) {
+    uint2 v;
+    v.x = bf16_bits(a) | (bf16_bits(b) << 16);
+    v.y = bf16_bits(c) | (bf16_bits(d) << 16);
+    *(uint2*)((uint16_t*)C + off) = v;
+  } else {
+    uint2 v;
+    v.x = f16_bits(a) | (f16_bits(b) << 16);
+    v.y = f16_bits(c) | (f16_bits(d) << 16);
+    *(uint2*)((uint16_t*)C + off) = v;
+  }
+}
+
+// Work item of one M-tile: its expert and its row range [row0, row0 + rows).
+struct TileRows {
+  int expert, row0, rows;
+};
+
+// Resolve M-tile t (tile map or dense), clamping device-side contents into range.
+__device__ __forceinline__ TileRows tile_rows(const int32_t* expert_ids, const int32_t* tile_offsets,
+                                              int t, int M, int tile_m, int num_experts) {
+  TileRows r;
+  if (expert_ids) {
+    r.expert = expert_ids[t];
+    int a = tile_offsets[t], b = tile_offsets[t + 1];
+    r.row0 = a;
+    r.rows = min(max(b - a, 0), tile_m);
+  } else {
+    r.expert = 0;
+    r.row0 = t * tile_m;
+    r.rows = min(tile_m, M - r.row0);
+  }
+  if (r.expert < 0 || r.expert >= num_experts || r.row0 < 0 || r.row0 >= M) {
+    r.rows = 0;
+  } else {
+    r.rows = min(r.rows, M - r.row0);
+  }
+  return r;
+}
+
+}  // namespace bsg

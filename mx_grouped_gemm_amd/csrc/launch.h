@@ -1,0 +1,33 @@
+// Internal launchers (C++ linkage) called by the C-ABI layer in bsgemm_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+struct GemmArgs {
+  const void* A;
+  const void* a_scales;
+  const void* B;
+  const void* b_scales;
+  const int32_t* expert_ids;    // nullptr: one dense group
+  const int32_t* tile_offsets;  // nullptr: one dense group
+  void* C;
+  int M, N, K;
+  int num_experts;
+  int num_tiles;  // M-tiles of 128 rows to visit
+};
+
+// Blockwise-FP8 (e4m3 x e4m3, fp32 1x128 / 128x128 scales). out: 1 f32, 2 bf16, 3 f16.
+hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream);
+
+// MX (e8m0 per 32 K). fmt_a / fmt_b: 1 e4m3, 2 e2m1. out: 1 f32, 2 bf16, 3 f16.
+hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream);
+
+// Token-to-expert tile map.
+hipError_t launch_build_tiles(const int32_t* counts, int num_experts, int num_tiles, int padded,
+                              int32_t* expert_offsets, int32_t* tile_offsets, int32_t* expert_ids,
+                              hipStream_t stream);
+
+}  // namespace bsg

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every input comes from the seeded generators in ``workloads``; expected values come only from
+``oracle``. Covers the tile map (bit-exact), the blockwise-FP8 grouped GEMM and the MX GEMM at
+small sizes spanning several tiles with ragged tails and edge cases, and the full workload
+sizes on sampled rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mx_grouped_gemm_amd as bsg
+from oracle import gemm as og
+from tests.parity import check, gpu_tile_map, poisoned, run_problem, sample_rows, say
+from workloads.generate import (MOE8, MOE32, blockwise_problem, make_problem, mx_problem,
+                                routing_counts)
+
+pytestmark = pytest.mark.gpu
+
+GPU = torch.cuda.is_available()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not GPU:
+        pytest.skip("no GPU")
+    say(f"\n[gpu-test] {request.node.name}")
+
+
+# --------------------------------------------------------------------------------------
+# tile map (a1): bit-exact
+# --------------------------------------------------------------------------------------
+TILE_CASES = [
+    ([3, 0, 130, 128], 6),
+    ([0, 0, 0], 2),
+    ([128, 256, 384], 6),          # exact multiples of 128
+    ([5000], 40),                  # all rows to one expert
+    ([1], 1),
+    ([300, 5], 2),                 # layout needs more tiles than given
+    ([7] * 4096, 4100),            # the expert limit
+]
+
+
+@pytest.mark.parametrize("padded", [True, False])
+@pytest.mark.parametrize("counts,T", TILE_CASES)
+def test_tile_map_bit_exact(counts, T, padded):
+    eo, to, ei = gpu_tile_map(counts, T, padded)
+    eo_r, to_r, ei_r = og.tile_map(counts, T, padded)
+    assert eo.cpu().numpy().tolist() == eo_r.tolist()
+    assert to.cpu().numpy().tolist() == to_r.tolist()
+    assert ei.cpu().numpy().tolist() == ei_r.tolist()
+
+
+@pytest.mark.parametrize("name", ["moe8", "moe32"])
+def test_tile_map_workload_routing(name):
+    counts = routing_counts(seed=0, **(MOE8 if name == "moe8" else MOE32))
+    T = int(np.sum(-(-counts // 128)))
+    for padded in (True, False):
+        eo, to, ei = gpu_tile_map(counts, T, padded)
+        eo_r, to_r, ei_r = og.tile_map(counts, T, padded)
+        assert np.array_equal(ei.cpu().numpy(), ei_r)
+        assert np.array_equal(to.cpu().numpy(), to_r)
+        assert np.array_equal(eo.cpu().numpy(), eo_r)
+
+
+# --------------------------------------------------------------------------------------
+# blockwise FP8 grouped GEMM
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_single_expert_128x256x512(out):
+    p = make_problem("single_128x256x512", device="cuda")
+    C, _, _ = run_problem(p, out)
+    check(p, out, C, label="single_128x256x512")
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 1024])
+def test_dense_k_depths(K):
+    """One, two and three K blocks exercise the pipeline prologue and drain."""
+    p = blockwise_problem(None, 256, K, device="cuda", a_rows=256, seed=K)
+    C, _, _ = run_problem(p, "f32")
+    check(p, "f32", C, label=f"dense K={K}")
+
+
+def test_dense_ragged_m_and_n_tail():
+    """M not a multiple of 128 (ragged last tile) and N with a half-empty 256-column block."""
+    p = blockwise_problem(None, 384, 512, device="cuda", a_rows=200, seed=3)
+    C, _, _ = run_problem(p, "bf16")
+    check(p, "bf16", C, label="dense M=200 N=384")
+
+
+def test_grouped_padded_with_empty_experts():
+    counts = [5, 0, 130, 17, 0, 300]
+    p = blockwise_problem(counts, 256, 640, device="cuda", seed=4)
+    C, _, _ = run_problem(p, "bf16")
+    check(p, "bf16", C, label="grouped padded")
+    # padding rows of expert 0 (rows 5..127) are exactly zero
+    assert torch.all(C[5:128].float() == 0)
+
+
+def test_grouped_compact_ragged_tiles():
+    """Unpadded layout: every expert's last tile is ragged; C rows of other experts untouched."""
+    counts = [70, 0, 200, 129, 1]
+    total = sum(counts)
+    E, N, K = len(counts), 384, 384
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    from workloads.generate import quantize_e4m3_rowblocks, quantize_e4m3_tiles
+    qa, sa = quantize_e4m3_rowblocks(torch.randn(total, K, generator=gen, device="cuda"))
+    qb, sb = quantize_e4m3_tiles(torch.randn(E, N, K, generator=gen, device="cuda"))
+    T = int(sum(-(-c // 128) for c in counts)) + 2          # two spare tiles stay -1
+    _, to, ei = gpu_tile_map(counts, T, padded=False)
+    C = poisoned(total, N, "f32")
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "f32")
+    bsg.bsgemm_grouped(qa, sa, qb, sb, ei, to, C, total, N, K, fmt, num_experts=E)
+
+    class P:  # minimal problem view for check()
+        pass
+    p = P()
+    p.qa, p.a_scales, p.qb, p.b_scales = qa, sa, qb, sb
+    p.scale_kind, p.fmt_a, p.fmt_b, p.M, p.N, p.K, p.counts = "blockwise", "e4m3", "e4m3", total, N, K, None
+    _, to_r, ei_r = og.tile_map(counts, T, padded=False)
+    check(p, "f32", C, tile_map_ref=(ei_r, to_r), label="grouped compact")
+
+
+def test_skipped_tiles_leave_output_untouched():
+    counts = [100, 40]
+    p = blockwise_problem(counts, 256, 256, device="cuda", seed=5)
+    T = p.M // 128 + 3                                         # trailing tiles get id -1
+    _, to, ei = gpu_tile_map(counts, T)
+    C = poisoned(p.M + 3 * 128, p.N, "bf16")
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
+    # A / a_scales need rows for every tile the map could name: pad them with zeros
+    qa = torch.cat([p.qa, torch.zeros(3 * 128, p.K, dtype=torch.uint8, device="cuda")])
+    sa = torch.cat([p.a_scales, torch.ones(3 * 128, p.K // 128, device="cuda")])
+    bsg.bsgemm_grouped(qa, sa, p.qb, p.b_scales, ei, to, C, qa.shape[0], p.N, p.K, fmt, num_experts=2)
+    assert torch.all(torch.isnan(C[p.M:].float()))
+    assert torch.all(torch.isfinite(C[:p.M].float()))
+
+
+def test_out_of_range_expert_ids_are_skipped():
+    p = blockwise_problem([128, 128], 256, 256, device="cuda", seed=6)
+    ei = torch.tensor([1, 7], dtype=torch.int32, device="cuda")   # 7 >= num_experts
+    to = torch.tensor([0, 128, 256], dtype=torch.int32, device="cuda")
+    C = poisoned(p.M, p.N, "f32")
+    bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei, to, C, p.M, p.N, p.K,
+                       bsg.make_fmt("e4m3", "e4m3", "blockwise", "f32"), num_experts=2)
+    assert torch.all(torch.isnan(C[128:]))
+    ref = og.blockwise_grouped(*(t.cpu().numpy() for t in (p.qa, p.a_scales, p.qb, p.b_scales)),
+                               np.array([1, -1]), np.array([0, 128, 256]))
+    den = og.blockwise_grouped_dequant(*(t.cpu().numpy() for t in (p.qa, p.a_scales, p.qb, p.b_scales)),
+                                       np.array([1, -1]), np.array([0, 128, 256]), absolute=True)
+    assert og.relative_error(C[:128].cpu().numpy(), ref[:128], den[:128]) <= 1e-3
+
+
+def test_exact_products_are_bit_exact():
+    """Operand layout pin: small-integer e4m3 values and power-of-two scales make every partial
+    and promoted sum exact in fp32, so the fp32 output must equal the oracle bit for bit."""
+    g = torch.Generator(device="cpu").manual_seed(21)
+    M, N, K = 256, 512, 512
+    # codes of the integers -4..4 in e4m3: 0x00, 0x38 (1), 0x40 (2), 0x44 (3), 0x48 (4), sign 0x80
+    mags = torch.tensor([0x00, 0x38, 0x40, 0x44, 0x48], dtype=torch.uint8)
+    def codes(*shape):
+        c = mags[torch.randint(0, 5, shape, generator=g)]
+        return c | (torch.randint(0, 2, shape, generator=g, dtype=torch.uint8) << 7)
+    qa, qb = codes(M, K), codes(1, N, K)
+    sa = torch.pow(2.0, torch.randint(-3, 4, (M, K // 128), generator=g).float())
+    sb = torch.pow(2.0, torch.randint(-3, 4, (1, N // 128, K // 128), generator=g).float())
+    C = poisoned(M, N, "f32")
+    bsg.bsgemm_grouped(qa.cuda(), sa.cuda(), qb.cuda(), sb.cuda(), None, None, C, M, N, K,
+                       bsg.make_fmt("e4m3", "e4m3", "blockwise", "f32"))
+    ref = og.blockwise_grouped(qa.numpy(), sa.numpy(), qb.numpy(), sb.numpy())
+    got = C.cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got != ref)
+    say(f"[exact] mismatches={len(bad)}")
+    assert len(bad) == 0, f"first mismatches at {bad[:5].tolist()}"
+
+
+def test_deterministic():
+    p = blockwise_problem([300, 200, 0, 90], 512, 1024, device="cuda", seed=7)
+    C1, _, _ = run_problem(p, "bf16")
+    C2, _, _ = run_problem(p, "bf16")
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+def test_dense_4096_with_outliers():
+    p = make_problem("dense_4096", device="cuda")
+    C, _, _ = run_problem(p, "bf16")
+    check(p, "bf16", C, label="dense_4096")
+
+
+def test_moe8_full():
+    p = make_problem("moe8_n2048_k4096", device="cuda")
+    C, _, _ = run_problem(p, "bf16")
+    check(p, "bf16", C, label="moe8_n2048_k4096")
+
+
+@pytest.mark.parametrize("name", ["moe32_gate_up_n4096_k7168", "moe32_down_n7168_k2048"])
+def test_moe32_full_size_sampled(name):
+    """Full size, same launch as the benchmark; the oracle checks two rows per M-tile, and every
+    row of a live tile must be finite (padding rows exactly zero)."""
+    p = make_problem(name, device="cuda")
+    C, ei, to = run_problem(p, "bf16")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(C).all()), "non-finite output"
+    rows = sample_rows(p, per_tile=2)
+    check(p, "bf16", C, rows=rows, label=name)
+    del C, p
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------------------
+# MX
+# --------------------------------------------------------------------------------------
+MX_PAIRS = [("e4m3", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e4m3"), ("e2m1", "e2m1")]
+
+
+@pytest.mark.parametrize("fa,fb", MX_PAIRS)
+@pytest.mark.parametrize("out", ["f16", "f32"])
+def test_mx_small(fa, fb, out):
+    p = mx_problem(256, 512, 640, fa, fb, device="cuda", seed=11)
+    C, _, _ = run_problem(p, out)
+    check(p, out, C, label=f"mx {fa}x{fb}")
+
+
+@pytest.mark.parametrize("fa,fb", MX_PAIRS)
+def test_mx_exact_products_bit_exact(fa, fb):
+    """Layout pin for elements, nibble order and per-32 scales: small values and scales near 1
+    keep every sum exact in fp32, so the fp32 output must equal the oracle bit for bit."""
+    g = torch.Generator(device="cpu").manual_seed(31)
+    M, N, K = 128, 256, 512
+
+    def elems(rows, f):
+        if f == "e4m3":
+            mags = torch.tensor([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44], dtype=torch.uint8)  # 0,.5,1,1.5,2,3
+            c = mags[torch.randint(0, 6, (rows, K), generator=g)]
+            return c | (torch.randint(0, 2, (rows, K), generator=g, dtype=torch.uint8) << 7)
+        return torch.randint(0, 256, (rows, K // 2), generator=g, dtype=torch.uint8)
+
+    qa, qb = elems(M, fa), elems(N, fb)
+    sa = torch.randint(125, 130, (M, K // 32), generator=g, dtype=torch.uint8)
+    sb = torch.randint(125, 130, (N, K // 32), generator=g, dtype=torch.uint8)
+    C = poisoned(M, N, "f32")
+    bsg.bsgemm_grouped(qa.cuda(), sa.cuda(), qb[None].cuda(), sb[None].cuda(), None, None, C, M, N, K,
+                       bsg.make_fmt(fa, fb, "mx", "f32"))
+    ref = og.mx_gemm(qa.numpy(), sa.numpy(), qb.numpy(), sb.numpy(), fa, fb)
+    got = C.cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got != ref)
+    say(f"[mx-exact] {fa}x{fb} mismatches={len(bad)}")
+    assert len(bad) == 0, f"first mismatches at {bad[:5].tolist()}"
+
+
+def test_mx_grouped():
+    """MX scales through the tile map (grouped), two experts."""
+    from workloads.generate import quantize_mx
+    counts = [130, 100]
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    starts = [0, 256]
+    M, N, K = 384, 256, 256
+    qa = torch.zeros(M, K, dtype=torch.uint8, device="cuda")
+    sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda")
+    for s, c in zip(starts, counts):
+        q, sc = quantize_mx(torch.randn(c, K, generator=gen, device="cuda"), "e4m3")
+        qa[s:s + c], sa[s:s + c] = q, sc
+    qb, sb = quantize_mx(torch.randn(2, N, K, generator=gen, device="cuda"), "e4m3")
+    _, to, ei = gpu_tile_map(counts, 3)
+    C = poisoned(M, N, "f16")
+    bsg.bsgemm_grouped(qa, sa, qb, sb, ei, to, C, M, N, K, bsg.make_fmt("e4m3", "e4m3", "mx", "f16"),
+                       num_experts=2)
+
+    class P:
+        pass
+    p = P()
+    p.qa, p.a_scales, p.qb, p.b_scales = qa, sa, qb, sb
+    p.scale_kind, p.fmt_a, p.fmt_b, p.M, p.N, p.K, p.counts = "mx", "e4m3", "e4m3", M, N, K, counts
+    check(p, "f16", C, label="mx grouped")
+
+
+@pytest.mark.parametrize("name", ["mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1"])
+def test_mx8192_sampled(name):
+    p = make_problem(name, device="cuda")
+    C, _, _ = run_problem(p, "f16")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(C).all())
+    rows = sample_rows(p, per_tile=2)
+    check(p, "f16", C, rows=rows, label=name)
