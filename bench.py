@@ -41,7 +41,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(problems, n_experts=8, rows_per_expert=64):
+def cpu_baseline(problems, n_experts=16, rows_per_expert=128):
     """Time the oracle on a bounded sample: ``rows_per_expert`` real rows of each of the first
     ``n_experts`` non-empty experts of the gate_up GEMM. Returns the JSON object."""
     from threadpoolctl import threadpool_info

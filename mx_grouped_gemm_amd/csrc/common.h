@@ -21,6 +21,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until this wave's LDS reads (and scalar loads) have completed: lgkmcnt(0), vmcnt and
+// expcnt left at their maxima.
+__device__ __forceinline__ void wait_lds_reads() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Workgroup barrier without the memory fence __syncthreads() adds (which would also wait for
 // every outstanding prefetch). Callers wait for exactly the loads they need first.
 __device__ __forceinline__ void barrier() {
@@ -39,6 +45,24 @@ __device__ __forceinline__ void g2lds4(const void* g, lds_void* lds) {
 }
 
 __device__ __forceinline__ lds_void* as_lds(uint8_t* p) { return (lds_void*)p; }
+
+// Raw buffer resource over [base, base + bytes): loads through it take a 32-bit per-lane offset
+// (VGPR) plus a wave-uniform offset (SGPR), and reads past `bytes` return zero instead of
+// touching memory. Word 3 selects 32-bit untyped data (gfx9 layout).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0xffffffffull ? (int)0xffffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Buffer -> LDS copies (buffer_load_dword{,x4} ... lds): lane i's bytes land at lds + i * size.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          lds_void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         lds_void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ v4i lds_read16(const uint8_t* p) { return *(const v4i*)p; }
 
@@ -85,6 +109,28 @@ __device__ __forceinline__ void store4(void* C, size_t off, float a, float b, fl
     *(uint2*)((uint16_t*)C + off) = v;
   }
 }
+
+// Work order. Blocks are dispatched round-robin over the 8 XCDs (each with its own L2), so
+// block b runs on XCD b % 8. The grid is a multiple of 8 and block b takes logical item
+// (b % 8) * (grid / 8) + b / 8: the blocks resident on one XCD work on consecutive logical
+// items. Logical items walk groups of `group_m` M-tiles, column block by column block, so the
+// items in flight on an XCD share A rows and B columns in its L2. Returns false for padding
+// blocks past the last item.
+__device__ __forceinline__ bool work_item(int num_tiles, int n_blocks, int group_m, int& t, int& nb) {
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int L = (b % 8) * (grid / 8) + b / 8;
+  if (L >= num_tiles * n_blocks) return false;
+  const int per_group = group_m * n_blocks;
+  const int g = L / per_group, r = L % per_group;
+  const int t0 = g * group_m;
+  const int gm = min(group_m, num_tiles - t0);
+  nb = r / gm;
+  t = t0 + r % gm;
+  return true;
+}
+
+// Grid size for `items` work items: rounded up to a multiple of 8 (see work_item).
+inline unsigned grid_for(long long items) { return (unsigned)((items + 7) / 8 * 8); }
 
 // Work item of one M-tile: its expert and its row range [row0, row0 + rows).
 struct TileRows {

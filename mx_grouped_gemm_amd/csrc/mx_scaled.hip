@@ -128,8 +128,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = blockIdx.x / n_blocks;
-  const int n0 = (blockIdx.x % n_blocks) * BN;
+  int t, nb;
+  if (!work_item(p.num_tiles, n_blocks, 8, t, nb)) return;
+  const int n0 = nb * BN;
   const TileRows tr = tile_rows(p.expert_ids, p.tile_offsets, t, p.M, BM, p.num_experts);
   if (tr.rows <= 0) return;
   const int e = tr.expert, row0 = tr.row0, rows = tr.rows;
@@ -222,8 +223,8 @@ hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream
   const int n_blocks = (a.N + BN - 1) / BN;
   const long long blocks = (long long)a.num_tiles * n_blocks;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks);
+  if (blocks > 0x7ffffff0LL) return hipErrorInvalidValue;
+  const dim3 grid(grid_for(blocks));
   if (fmt_a == 1 && fmt_b == 1) return launch_fmt<1, 1>(a, out, stream, grid, n_blocks);
   if (fmt_a == 1 && fmt_b == 2) return launch_fmt<1, 2>(a, out, stream, grid, n_blocks);
   if (fmt_a == 2 && fmt_b == 1) return launch_fmt<2, 1>(a, out, stream, grid, n_blocks);
