@@ -75,7 +75,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(each GPU would run its own experts' share; see DESIGN.md)", file=sys.stderr)
+              "(under expert parallelism each GPU runs this GEMM on its own experts' share)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

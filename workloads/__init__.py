@@ -6,7 +6,7 @@ imports neither the oracle nor the library. Both sides consume the same bytes.
 """
 
 from .generate import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Problem,
     make_problem,
     quantize_e4m3_rowblocks,

@@ -225,24 +225,24 @@ def _mx_problem(name, M, N, K, fmt_a, fmt_b, device, seed):
 MOE8 = dict(tokens=4096, top_k=2, experts=8, alpha=0.5, n_empty=0)
 MOE32 = dict(tokens=16384, top_k=8, experts=32, alpha=1.0, n_empty=2)
 
-CONFIGS = {
-    # 0: one expert, 128 x 256 x 512, fp32 and bf16 output
+WORKLOADS = {
+    # one expert, 128 x 256 x 512, fp32 and bf16 output
     "single_128x256x512": lambda dev, seed: _blockwise_problem(
         "single_128x256x512", None, 256, 512, 1, ("f32", "bf16"), dev, seed, a_rows=128),
-    # 1: one dense group 4096^3, every 64th row of A and of B scaled x100, bf16 output
+    # one dense group 4096^3, every 64th row of A and of B scaled x100, bf16 output
     "dense_4096": lambda dev, seed: _blockwise_problem(
         "dense_4096", None, 4096, 4096, 1, ("bf16",), dev, seed, outlier_every=64, a_rows=4096),
-    # 2: 8 experts, 4096 tokens top-2, Dirichlet(0.5), N=2048, K=4096, bf16
+    # 8 experts, 4096 tokens top-2, Dirichlet(0.5), N=2048, K=4096, bf16
     "moe8_n2048_k4096": lambda dev, seed: _blockwise_problem(
         "moe8_n2048_k4096", routing_counts(seed=seed, **MOE8), 2048, 4096, 8, ("bf16",), dev, seed),
-    # 3: 32 local experts, 16384 tokens top-8, Dirichlet(1.0), two experts empty, bf16
+    # 32 local experts, 16384 tokens top-8, Dirichlet(1.0), two experts empty, bf16
     "moe32_gate_up_n4096_k7168": lambda dev, seed: _blockwise_problem(
         "moe32_gate_up_n4096_k7168", routing_counts(seed=seed, **MOE32), 4096, 7168, 32, ("bf16",),
         dev, seed),
     "moe32_down_n7168_k2048": lambda dev, seed: _blockwise_problem(
         "moe32_down_n7168_k2048", routing_counts(seed=seed, **MOE32), 7168, 2048, 32, ("bf16",),
         dev, seed + 1),
-    # 4: MX 8192^3, three element-format pairs, fp16 output
+    # MX 8192^3, three element-format pairs, fp16 output
     "mx8192_e4m3_e4m3": lambda dev, seed: _mx_problem("mx8192_e4m3_e4m3", 8192, 8192, 8192,
                                                       "e4m3", "e4m3", dev, seed),
     "mx8192_e4m3_e2m1": lambda dev, seed: _mx_problem("mx8192_e4m3_e2m1", 8192, 8192, 8192,
@@ -254,7 +254,7 @@ CONFIGS = {
 
 def make_problem(name, device="cpu", seed=0):
     """Build a named workload on ``device``."""
-    return CONFIGS[name](device, seed)
+    return WORKLOADS[name](device, seed)
 
 
 def blockwise_problem(counts, N, K, device="cpu", seed=0, a_rows=None, E=None, outlier_every=0,
