@@ -13,9 +13,11 @@ per-launch time is measured with HIP events on the stream the kernels run on, an
 oracle's rate on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration MIB --steps K   (HBM counter calibration)
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +32,18 @@ PEAK_FP8_TFLOPS = 5033.0   # MI355X dense FP8 MFMA peak (256 CU x 2.4 GHz x 8192
 PEAK_HBM_GBS = 8000.0
 METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 
+# HBM bytes per gate_up launch: rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
+# 1 GiB device copy measured with the same counters). Valid only for the kernel source whose
+# sha256 starts with this prefix; reported as null for any other source.
+GATE_UP_TRAFFIC = ("f82a9ca744fc0328", 12.51e9)
+KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
+
+
+def measured_traffic():
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return GATE_UP_TRAFFIC[1] if digest.startswith(GATE_UP_TRAFFIC[0]) else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -38,6 +52,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run --steps device-to-device copies of MIB "
+                         "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
     return ap.parse_args()
 
 
@@ -80,6 +97,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
 
     import mx_grouped_gemm_amd as bsg
     from workloads.generate import make_problem
@@ -169,7 +197,8 @@ def main():
         "roofline": {
             "kernel": "bw_fp8_grouped_kernel (gate_up launch)",
             "bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": measured_traffic(),
         },
     }
     if not args.no_cpu_baseline:

@@ -9,202 +9,92 @@
 // then converts acc to the output type.
 //
 // CDNA4 mapping (not the pages' Blackwell design):
-//  * block = 8 waves (2 per SIMD), tile 128 (M) x 256 (N); each wave owns 64 x 64 as 2 x 2
-//    fragments of 32 x 32. A 128-wide K block is two v_mfma_scale_f32_32x32x64_f8f6f4 (scale
-//    operands neutral), one per 64-wide K half, chained into a fresh fp32 partial P in VGPRs;
-//    the promote is 16 FMAs per lane per fragment into VGPR accumulators.
-//  * ping-pong schedule: waves 0-3 (group 0, rows 0-63) and 4-7 (group 1, rows 64-127) put one
-//    wave of each group on every SIMD and run half a K block out of phase around the single
-//    barrier per K block. Group 0 issues the MFMAs of block b, passes barrier b, then promotes
-//    b and reads block b+1; group 1 promotes b-1 and reads b, passes barrier b, then issues
-//    the MFMAs of b. Between two barriers each SIMD holds one wave feeding the matrix unit and
-//    one wave doing the VALU promotion and LDS reads, and the two overlap.
-//  * operands stream through a 3-stage LDS ring filled by buffer -> LDS copies
-//    (buffer_load_dwordx4 ... lds) that group 0 issues three K blocks ahead; 16-byte chunks are
-//    XOR-swizzled so fragment reads are free of bank conflicts. The scales ride in the same
-//    ring: 128 A scales (one per row) and the block's B scales (one per 128 columns).
+//  * block tile 256 (M) x 256 (N): two consecutive 128-row M-tiles of one expert (a lone tile,
+//    or a pair whose experts differ, runs as one or two 128-row passes). The copy traffic per
+//    flop of a 256 x 256 tile is two thirds of a 128 x 256 one; the L2 -> LDS copy path
+//    (a bounded number of outstanding line requests per CU) is what limits this kernel.
+//  * 8 waves (2 per SIMD), each owning 64 x 128 as 4 x 8 fragments of 16 x 16. One
+//    v_mfma_scale_f32_16x16x128_f8f6f4 (scale operands neutral) computes a fragment's whole
+//    128-wide K block, so the partial P is 4 registers and is promoted (4 FMAs) two MFMAs
+//    after it was issued; the 4 A fragments stay in registers for the K block, the 8 B
+//    fragments stream through a 3-deep register queue two fragments ahead of their MFMAs.
+//  * operands stream through a 2-stage LDS ring filled by buffer -> LDS copies
+//    (buffer_load_dwordx4 ... lds); 16-byte chunks are XOR-swizzled so fragment reads are free
+//    of bank conflicts. One barrier per K block, after the last read of the block's stage: the
+//    copies of block b+2 then refill that stage while the last B fragment's MFMAs run and the
+//    A fragments of block b+1 are read.
+//  * A scales: each tile's rows are staged 8 K blocks at a time (256 rows x 8 floats, double
+//    buffered), so a 128-byte line of the row-major a_scales serves 8 K blocks instead of one.
+//    The B scale of each of the two 128-column blocks rides in the stage.
 //  * the MFMA computes C^T fragments (B rows as the first operand) so that each lane holds 4
 //    consecutive output columns of one row: the epilogue writes 8-byte (bf16/fp16) or 16-byte
-//    (fp32) vectors.
+//    (fp32) vectors, and each lane needs one A scale per M fragment.
 #include "common.h"
 #include "launch.h"
 
 namespace bsg {
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 128;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128, TILE_M = 128;
 constexpr int NWAVES = 8, NTHREADS = NWAVES * kWave;
-constexpr int NCOPY = 4;                                    // waves issuing the copies (group 0)
-constexpr int WAVE_M = 64, WAVE_N = 64;                     // wave tile: 2 x 2 fragments
-constexpr int FM = WAVE_M / 32, FN = WAVE_N / 32;
-constexpr int STAGES = 3;
-constexpr int A_BYTES = BM * BK;                            // 16 KiB
-constexpr int B_BYTES = BN * BK;                            // 32 KiB
-// scale strip: copy wave w owns 64 floats at SS_OFF + 256 w; floats 0..31 are the A scales of
-// rows 32w..32w+31 and float 32 is the B scale of the 64-column block w (of its 128 columns)
-constexpr int SS_OFF = A_BYTES + B_BYTES;
-constexpr int SS_BYTES = NCOPY * 64 * 4;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SS_BYTES;   // 50176
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;             // 150528 of 160 KiB
-constexpr int A_INSTR = A_BYTES / 1024 / NCOPY;             // 1 KiB copies per copy wave
-constexpr int B_INSTR = B_BYTES / 1024 / NCOPY;
-constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR + 2;      // + A-scale and B-scale copies
+constexpr int WM = 64, WN = 128;                  // wave tile
+constexpr int MI = WM / 16, NJ = WN / 16;         // 4 x 8 fragments of 16 x 16
+constexpr int STAGES = 2;
+constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;          // 32 KiB each per stage
+constexpr int A_REGION = 0;
+constexpr int B_REGION = STAGES * A_BYTES;                   // 64 KiB
+constexpr int BS_REGION = B_REGION + STAGES * B_BYTES;       // 128 KiB: B scales, per stage
+constexpr int BS_BYTES = 512;                                // 64 copies of each column block's scale
+constexpr int AS_REGION = BS_REGION + STAGES * BS_BYTES;     // A scale chunks
+constexpr int AS_CHUNK = 8;                                  // K blocks per A scale chunk
+constexpr int AS_BYTES = BM * AS_CHUNK * 4;                  // 8 KiB per chunk
+constexpr int LDS_BYTES = AS_REGION + 2 * AS_BYTES;          // 148480 of 160 KiB
+constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;             // 4
+constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;             // 4
+constexpr int AS_INSTR = AS_BYTES / 256 / NWAVES;            // 4 (4-byte copies, 64 lanes)
 
-// Per-thread copy plan of one stage (lane i of a 1 KiB instruction covers row i/8, 16-byte
-// slot i%8 of that row). Sources are buffer resources over the block's rows (wave-uniform,
-// scalar registers) plus 32-bit per-lane offsets; a K block advances the scalar offset only.
-// Rows past the tile (ragged M) or past N read as zero through the resource bounds.
 struct LoadPlan {
-  __amdgpu_buffer_rsrc_t a_rsrc;   // A rows of the tile
-  __amdgpu_buffer_rsrc_t b_rsrc;   // B[e] rows of the column block
-  __amdgpu_buffer_rsrc_t as_rsrc;  // a_scales rows of the tile
-  __amdgpu_buffer_rsrc_t bs_rsrc;  // b_scales[e] row of this wave's 64-column block
-  uint32_t a_off[A_INSTR], b_off[B_INSTR], as_off;
-  int a_dst[A_INSTR], b_dst[B_INSTR], ss_dst;
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, bs_rsrc, as_rsrc;
+  uint32_t voff[A_INSTR];  // data copies: per-lane offset of instruction i (same for A and B)
+  uint32_t as_voff;      // A scale chunk: lane part (row and column inside the chunk)
+  uint32_t as_row8;      // A scale chunk: bytes of 8 rows of a_scales
+  int a_dst, b_dst;
 };
 
-
-// Fragment read offsets inside a stage.
-struct FragPlan {
-  int a_off[FM][2][2];  // [m fragment][K half][16-byte half]
-  int b_off[FN][2][2];  // [n fragment][K half][16-byte half]
-  int as_off[FM];       // A scale of the lane's row, per m fragment
-  int bs_off;           // B scale of the wave's column block
-};
-
-// Fragments of one K block: both 64-wide halves, 32 bytes per lane per fragment half.
-struct Frags {
-  v8i a[FM][2];
-  v8i b[FN][2];
-};
-
-// The stage's scales for this lane, kept raw: the product is formed where it is used.
-struct Scales {
-  float a[FM];
-  float b;
-};
-
-__device__ __forceinline__ void issue_stage(uint8_t* dst, const LoadPlan& lp, int kb, int lane) {
-  kb = __builtin_amdgcn_readfirstlane(kb);                     // uniform: scalar offsets
-  const uint32_t koff = (uint32_t)kb * BK, soff = (uint32_t)kb * 4;
+// Copies of K block kb into one stage; every AS_CHUNK-th call also stages the A scales of the
+// chunk that starts AS_CHUNK blocks later.
+__device__ __forceinline__ void issue_stage(uint8_t* __restrict__ da, uint8_t* __restrict__ db,
+                                            uint8_t* __restrict__ dbs, const LoadPlan& lp, int kb,
+                                            int wave) {
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  const uint32_t koff = (uint32_t)kb * BK;
 #pragma unroll
-  for (int i = 0; i < A_INSTR; i++) buf2lds16(lp.a_rsrc, lp.a_off[i], koff, as_lds(dst + lp.a_dst[i]));
+  for (int i = 0; i < A_INSTR; i++)
+    buf2lds16(lp.a_rsrc, lp.voff[i], koff, as_lds(da + lp.a_dst + i * 1024));
 #pragma unroll
-  for (int i = 0; i < B_INSTR; i++) buf2lds16(lp.b_rsrc, lp.b_off[i], koff, as_lds(dst + lp.b_dst[i]));
-  if (lane < 32) buf2lds4(lp.as_rsrc, lp.as_off, soff, as_lds(dst + lp.ss_dst));
-  if (lane == 32) buf2lds4(lp.bs_rsrc, 0, soff, as_lds(dst + lp.ss_dst));
+  for (int i = 0; i < B_INSTR; i++)
+    buf2lds16(lp.b_rsrc, lp.voff[i], koff, as_lds(db + lp.b_dst + i * 1024));
+  if (wave < 2) buf2lds4(lp.bs_rsrc, 0, (uint32_t)kb * 4, as_lds(dbs + wave * 256));
 }
 
-// Read one K half (kh) of the block's fragments from a stage.
-__device__ __forceinline__ void read_half(const uint8_t* st, const FragPlan& fp, int kh, Frags& f) {
+__device__ __forceinline__ void issue_scale_chunk(uint8_t* __restrict__ dst, const LoadPlan& lp,
+                                                  int chunk, int wave) {
+  const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * AS_CHUNK * 4;
 #pragma unroll
-  for (int i = 0; i < FM; i++)
-    f.a[i][kh] = cat(lds_read16(st + fp.a_off[i][kh][0]), lds_read16(st + fp.a_off[i][kh][1]));
-#pragma unroll
-  for (int j = 0; j < FN; j++)
-    f.b[j][kh] = cat(lds_read16(st + fp.b_off[j][kh][0]), lds_read16(st + fp.b_off[j][kh][1]));
+  for (int i = 0; i < AS_INSTR; i++)
+    buf2lds4(lp.as_rsrc, lp.as_voff + col + i * lp.as_row8, 0,
+             as_lds(dst + (wave * AS_INSTR + i) * 256));
 }
 
-__device__ __forceinline__ void read_frags(const uint8_t* st, const FragPlan& fp, Frags& f) {
-  read_half(st, fp, 0, f);
-  read_half(st, fp, 1, f);
+__device__ __forceinline__ v8i read_frag(const uint8_t* p, const int (&base)[2]) {
+  return cat(lds_read16(p + base[0]), lds_read16(p + base[1]));
 }
 
-__device__ __forceinline__ void read_scales(const uint8_t* st, const FragPlan& fp, Scales& sc) {
-  sc.b = *(const float*)(st + fp.bs_off);
-#pragma unroll
-  for (int i = 0; i < FM; i++) sc.a[i] = *(const float*)(st + fp.as_off[i]);
-}
-
-// The K block's fresh partial of every fragment: the two K halves chained.
-__device__ __forceinline__ void mma_block(const Frags& f, v16f (&part)[FM][FN]) {
-  const v16f zero = (v16f){};
-#pragma unroll
-  for (int mi = 0; mi < FM; mi++)
-#pragma unroll
-    for (int ni = 0; ni < FN; ni++)
-      part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni][0], f.a[mi][0], zero,
-                                                                    0, 0, 0, 127, 0, 127);
-#pragma unroll
-  for (int mi = 0; mi < FM; mi++)
-#pragma unroll
-    for (int ni = 0; ni < FN; ni++)
-      part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni][1], f.a[mi][1],
-                                                                    part[mi][ni], 0, 0, 0, 127,
-                                                                    0, 127);
-  // keep the MFMAs in this phase (not sunk past the barrier to their use)
-#pragma unroll
-  for (int mi = 0; mi < FM; mi++)
-#pragma unroll
-    for (int ni = 0; ni < FN; ni++) asm volatile("" : "+v"(part[mi][ni]));
-}
-
-__device__ __forceinline__ void promote(const v16f (&part)[FM][FN], const Scales& sc,
-                                        v16f (&acc)[FM][FN]) {
-#pragma unroll
-  for (int mi = 0; mi < FM; mi++) {
-    const float s = sc.a[mi] * sc.b;
-#pragma unroll
-    for (int ni = 0; ni < FN; ni++) acc[mi][ni] += part[mi][ni] * s;
-  }
-}
-
-// Wait until this wave's copies of the stage about to be published have landed: the copies of
-// the following K block (if issued) may stay in flight.
-__device__ __forceinline__ void wait_vmcnt_for(bool following_in_flight) {
-  if (following_in_flight) wait_vmcnt<LOADS_PER_STAGE>(); else wait_vmcnt<0>();
-}
-
-// Refill order. A fragment register may only be overwritten once the MFMAs reading it have
-// finished, or the LDS read stalls on them. The first-half MFMAs of a block are issued first,
-// so the first-half registers are refilled first; the second half is refilled after the
-// promotion, which itself waits for all of this wave's MFMAs to complete.
-
-// Group 0, K block b: MFMAs of b (operands in f); barrier b (its copies of stage b+1 have
-// landed, its reads of stage b are done); copies of block b+3 into stage b's slot; refill the
-// first half from block b+1; promote b; refill the second half. `next_st` (stage b+1) and
-// `cur_st` (stage b) are distinct: __restrict__ lets the compiler keep the copies into cur_st
-// in flight across the reads of next_st (their completion is awaited before a later barrier).
-__device__ __forceinline__ void step_g0(const uint8_t* __restrict__ next_st, uint8_t* __restrict__ cur_st,
-                                        const LoadPlan& lp, const FragPlan& fp, int lane, int b,
-                                        int KB, Frags& f, Scales& sc, v16f (&acc)[FM][FN]) {
-  v16f part[FM][FN];
-  mma_block(f, part);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_for(b + 2 < KB);
-  wait_lds_reads();
-  barrier();
-  if (b + 3 < KB) issue_stage(cur_st, lp, b + 3, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  const Scales s_b = sc;
-  const bool more = b + 1 < KB;
-  if (more) {
-    read_half(next_st, fp, 0, f);
-    read_scales(next_st, fp, sc);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  promote(part, s_b, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  if (more) read_half(next_st, fp, 1, f);
-}
-
-// Group 1, K block b: refill the first half from block b (stage published at barrier b-1);
-// promote b-1 (partials in part); refill the second half; barrier b (its reads of stage b are
-// done); MFMAs of b. Group 1 issues no copies.
-__device__ __forceinline__ void step_g1(const uint8_t* st_b, const FragPlan& fp, int b, Frags& f,
-                                        Scales& sc, v16f (&part)[FM][FN], v16f (&acc)[FM][FN]) {
-  const Scales s_prev = sc;
-  read_half(st_b, fp, 0, f);
-  read_scales(st_b, fp, sc);
-  __builtin_amdgcn_sched_barrier(0);
-  if (b > 0) promote(part, s_prev, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  read_half(st_b, fp, 1, f);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_lds_reads();
-  barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  mma_block(f, part);
+__device__ __forceinline__ v4f mma(const v8i& b, const v8i& a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                          127, 0, 127);
 }
 
 template <int OUT>
@@ -213,121 +103,206 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int t, nb;
-  if (!work_item(p.num_tiles, n_blocks, 8, t, nb)) return;
-  const int n0 = nb * BN;
-  const TileRows tr = tile_rows(p.expert_ids, p.tile_offsets, t, p.M, BM, p.num_experts);
-  if (tr.rows <= 0) return;
-  // the tile's expert and rows are block-uniform: keep them in scalar registers
-  const int e = __builtin_amdgcn_readfirstlane(tr.expert);
-  const int row0 = __builtin_amdgcn_readfirstlane(tr.row0);
-  const int rows = __builtin_amdgcn_readfirstlane(tr.rows);
-  const int N = p.N, KB = p.K / BK;
+  const int num_super = (p.num_tiles + 1) / 2;
+  int s, nb;
+  if (!work_item(num_super, n_blocks, 8, s, nb)) return;
+  const int n0 = nb * BN, N = p.N, KB = p.K / BK;
   const size_t K = (size_t)p.K;
-  const uint8_t* A = (const uint8_t*)p.A;
-  const uint8_t* Be = (const uint8_t*)p.B + (size_t)e * N * K;
-  const float* a_scales = (const float*)p.a_scales;
-  const float* b_scales = (const float*)p.b_scales;
-  const bool group0 = wave < NCOPY;
-  const int wm = wave >> 2, wn = wave & 3;                     // rows 64 wm, cols 64 wn
+  const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
+  const int r16 = lane & 15, q = lane >> 4;
   const int ncols = min(BN, N - n0);
 
-  // ---- copy plan (group 0 only) ----
-  LoadPlan lp;
-  if (group0) {
+  // The two 128-row tiles of this super-tile: one 256-row pass when they are consecutive rows
+  // of one expert, else one pass per tile.
+  const TileRows t0 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s, p.M, TILE_M, p.num_experts);
+  TileRows t1 = {0, 0, 0};
+  if (2 * s + 1 < p.num_tiles)
+    t1 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s + 1, p.M, TILE_M, p.num_experts);
+  // pass 0 is (e0, r0, n0rows), pass 1 (if any) is (e1, r1, n1rows); all block-uniform
+  int e0 = t0.expert, r0 = t0.row0, n0rows = t0.rows, e1 = t1.expert, r1 = t1.row0, n1rows = t1.rows;
+  int npass;
+  if (t0.rows == TILE_M && t1.rows > 0 && t1.expert == t0.expert && t1.row0 == t0.row0 + TILE_M) {
+    n0rows = TILE_M + t1.rows;
+    npass = 1;
+  } else if (t0.rows > 0) {
+    npass = t1.rows > 0 ? 2 : 1;
+  } else {
+    e0 = e1; r0 = r1; n0rows = n1rows;
+    npass = t1.rows > 0 ? 1 : 0;
+  }
+
+  // per-lane LDS read bases: lane (r16, q) holds K bytes [32 q, 32 q + 32) of row r16 of a
+  // fragment (two 16-byte chunks); the swizzle of row 16 f + r16 depends on r16 only
+  const int sw = (r16 & 7) ^ ((r16 >> 3) & 1);
+  int base_a[2], base_b[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int chunk = ((2 * q + h) ^ sw) * 16;
+    base_a[h] = A_REGION + (wm * WM + r16) * BK + chunk;
+    base_b[h] = B_REGION + (wn * WN + r16) * BK + chunk;
+  }
+  const int base_as = AS_REGION + (wm * WM + r16) * AS_CHUNK * 4;
+  const int base_bs = BS_REGION + wn * 256;
+
+  for (int ps = 0; ps < npass; ps++) {
+    const int e = __builtin_amdgcn_readfirstlane(ps == 0 ? e0 : e1);
+    const int row0 = __builtin_amdgcn_readfirstlane(ps == 0 ? r0 : r1);
+    const int rows = __builtin_amdgcn_readfirstlane(ps == 0 ? n0rows : n1rows);
+    const uint8_t* A = (const uint8_t*)p.A;
+    const uint8_t* Be = (const uint8_t*)p.B + (size_t)e * N * K;
+
+    // Copy plan. Rows past the pass (ragged M) or past N read as zero through the resource
+    // bounds; so do scales past the end of a_scales.
+    LoadPlan lp;
     lp.a_rsrc = make_rsrc(A + (size_t)row0 * K, (uint64_t)rows * K);
     lp.b_rsrc = make_rsrc(Be + (size_t)n0 * K, (uint64_t)ncols * K);
-    lp.as_rsrc = make_rsrc(a_scales + (size_t)row0 * KB, (uint64_t)rows * KB * 4);
-    const int nb = min((n0 + wave * WAVE_N) / 128, N / 128 - 1);
-    lp.bs_rsrc = make_rsrc(b_scales + ((size_t)e * (N / 128) + nb) * KB, (uint64_t)KB * 4);
-    const int lrow = lane >> 3, slot = lane & 7;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; i++) {                        // wave w: A rows [32w, 32w+32)
-      const int r = (wave * A_INSTR + i) * 8 + lrow;
-      lp.a_off[i] = (uint32_t)(r * K + (slot ^ swz8(r)) * 16);
-      lp.a_dst[i] = (wave * A_INSTR + i) * 8 * BK;
+    {
+      const int cb = min(n0 / 128 + (wave & 1), N / 128 - 1);    // wave 0 / 1: column block 0 / 1
+      lp.bs_rsrc = make_rsrc((const float*)p.b_scales + ((size_t)e * (N / 128) + cb) * KB, (uint64_t)KB * 4);
     }
+    lp.as_rsrc = make_rsrc((const float*)p.a_scales + (size_t)row0 * KB, (uint64_t)rows * KB * 4);
+    {
+      const int lrow = lane >> 3, slot = lane & 7;
+      // Instruction i of wave w covers rows 32 w + 8 i + lrow (swz8 of that row is lrow ^ (i & 1)).
+      // The whole row offset sits in the per-lane offset, which the resource bounds check.
 #pragma unroll
-    for (int i = 0; i < B_INSTR; i++) {                        // wave w: B rows [64w, 64w+64)
-      const int r = (wave * B_INSTR + i) * 8 + lrow;
-      lp.b_off[i] = (uint32_t)(r * K + (slot ^ swz8(r)) * 16);
-      lp.b_dst[i] = A_BYTES + (wave * B_INSTR + i) * 8 * BK;
+      for (int i = 0; i < A_INSTR; i++)
+        lp.voff[i] = (uint32_t)((wave * 32 + i * 8 + lrow) * K + ((slot ^ lrow ^ (i & 1)) * 16));
+      lp.a_dst = wave * A_INSTR * 1024;
+      lp.b_dst = wave * B_INSTR * 1024;
+      // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow, column slot
+      lp.as_voff = (uint32_t)(((wave * 32 + lrow) * KB + slot) * 4);
+      lp.as_row8 = (uint32_t)(8 * KB * 4);
     }
-    lp.as_off = (uint32_t)((wave * 32 + (lane & 31)) * KB * 4);
-    lp.ss_dst = SS_OFF + wave * 64 * 4;
-  }
 
-  // ---- fragment read plan ----
-  FragPlan fp;
-  const int fr = lane & 31, kq = lane >> 5;
+    v4f acc[MI][NJ];
 #pragma unroll
-  for (int kh = 0; kh < 2; kh++)
+    for (int i = 0; i < MI; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = kh * 4 + kq * 2 + j;                       // 16-byte K chunk of this lane
+      for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // prologue: A scales of chunks 0 and 1, blocks 0 and 1 in flight; block 0 published
+    issue_scale_chunk(smem + AS_REGION, lp, 0, wave);
+    issue_scale_chunk(smem + AS_REGION + AS_BYTES, lp, 1, wave);
+    issue_stage(smem + A_REGION, smem + B_REGION, smem + BS_REGION, lp, 0, wave);
+    issue_stage(smem + A_REGION + A_BYTES, smem + B_REGION + B_BYTES, smem + BS_REGION + BS_BYTES,
+                lp, min(1, KB - 1), wave);
+    wait_vmcnt<0>();
+    barrier();
+
+    v8i af[MI], bq[3];
+    float as_raw[MI], bs_raw;
 #pragma unroll
-      for (int f = 0; f < FM; f++) {
-        const int ra = wm * WAVE_M + f * 32 + fr;
-        fp.a_off[f][kh][j] = ra * BK + ((c ^ swz8(ra)) * 16);
+    for (int i = 0; i < MI; i++) af[i] = read_frag(smem + i * 2048, base_a);
+    bq[0] = read_frag(smem, base_b);
+    bq[1] = read_frag(smem + 2048, base_b);
+#pragma unroll
+    for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + base_as + i * 16 * AS_CHUNK * 4);
+    bs_raw = *(const float*)(smem + base_bs);
+
+    for (int b = 0; b < KB; b++) {
+      const int S = b & 1;
+      const int so_ab = S * A_BYTES, so_bs = S * BS_BYTES;       // this block's stage
+      const int sn_ab = (S ^ 1) * A_BYTES, sn_bs = (S ^ 1) * BS_BYTES;
+      float sc[MI];
+#pragma unroll
+      for (int i = 0; i < MI; i++) sc[i] = as_raw[i] * bs_raw;
+      v4f part[3];
+      // passes 0..6: B fragment j against the 4 resident A fragments; B fragment j + 2 is read
+      // at the start of pass j. The promotion of each partial is pinned right after the MFMA two
+      // slots later, which also keeps the MFMAs in their pass.
+#pragma unroll
+      for (int j = 0; j < NJ - 1; j++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 2 < NJ) bq[(j + 2) % 3] = read_frag(smem + so_ab + (j + 2) * 2048, base_b);
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+          const int k = j * MI + i;
+          part[k % 3] = mma(bq[j % 3], af[i]);
+          if (k >= 2) {
+            const int kp = k - 2, jp = kp / MI, ip = kp % MI;
+            acc[ip][jp] += part[kp % 3] * sc[ip];
+            asm volatile("" : "+v"(acc[ip][jp]));
+          }
+        }
+        if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // This wave's reads of stage S are done and its copies of block b+1 have landed; after
+      // the barrier every wave's have, so block b+1 is readable and stage S is free.
+      wait_vmcnt<0>();
+      wait_lds_reads();
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
+      // MFMA, then the first two B fragments and the scales of block b+1 are read and the copies
+      // of block b+2 go into stage S (past the last block they repeat block KB-1 into a stage
+      // that is not read again).
 #pragma unroll
-      for (int f = 0; f < FN; f++) {
-        const int rb = wn * WAVE_N + f * 32 + fr;
-        fp.b_off[f][kh][j] = A_BYTES + rb * BK + ((c ^ swz8(rb)) * 16);
+      for (int i = 0; i < MI; i++) {
+        const int k = (NJ - 1) * MI + i;
+        part[k % 3] = mma(bq[(NJ - 1) % 3], af[i]);
+        {
+          const int kp = k - 2, jp = kp / MI, ip = kp % MI;
+          acc[ip][jp] += part[kp % 3] * sc[ip];
+          asm volatile("" : "+v"(acc[ip][jp]));
+        }
+        af[i] = read_frag(smem + sn_ab + i * 2048, base_a);
+      }
+      bq[0] = read_frag(smem + sn_ab, base_b);
+      bq[1] = read_frag(smem + sn_ab + 2048, base_b);
+      {
+        const int bn = min(b + 1, KB - 1);
+        const int as_off = ((bn / AS_CHUNK) & 1) * AS_BYTES + (bn % AS_CHUNK) * 4;
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+          as_raw[i] = *(const float*)(smem + base_as + as_off + i * 16 * AS_CHUNK * 4);
+      }
+      bs_raw = *(const float*)(smem + sn_bs + base_bs);
+      issue_stage(smem + A_REGION + so_ab, smem + B_REGION + so_ab, smem + BS_REGION + so_bs, lp,
+                  min(b + 2, KB - 1), wave);
+      // The A scales of chunk c+1 (blocks 8c+8..) replace those of chunk c-1 while block 8c is
+      // computed: chunk c-1 was last read for block 8c-1.
+      if (b % AS_CHUNK == 0 && b > 0)
+        issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
+                          wave);
+#pragma unroll
+      for (int i = 0; i < MI; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the last two partials of the block
+#pragma unroll
+      for (int k = MI * NJ - 2; k < MI * NJ; k++) {
+        const int jp = k / MI, ip = k % MI;
+        acc[ip][jp] += part[k % 3] * sc[ip];
+        asm volatile("" : "+v"(acc[ip][jp]));
       }
     }
-#pragma unroll
-  for (int f = 0; f < FM; f++) {
-    const int ra = wm * WAVE_M + f * 32 + fr;
-    fp.as_off[f] = SS_OFF + (ra >> 5) * 256 + (ra & 31) * 4;
-  }
-  fp.bs_off = SS_OFF + wn * 256 + 32 * 4;
+    wait_vmcnt<0>();
 
-  v16f acc[FM][FN];
+    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N
+    // fragment
 #pragma unroll
-  for (int i = 0; i < FM; i++)
+    for (int i = 0; i < MI; i++) {
+      const int mloc = wm * WM + i * 16 + r16;
+      if (mloc >= rows) continue;
+      const size_t crow = (size_t)(row0 + mloc) * N;
 #pragma unroll
-    for (int j = 0; j < FN; j++) acc[i][j] = (v16f){};
-
-  // prologue: group 0 puts K blocks 0, 1, 2 in flight; stage 0 published; group 0 holds block 0
-  if (group0) {
-    issue_stage(smem, lp, 0, lane);
-    if (KB > 1) issue_stage(smem + STAGE_BYTES, lp, 1, lane);
-    if (KB > 2) issue_stage(smem + 2 * STAGE_BYTES, lp, 2, lane);
-    if (KB > 2) wait_vmcnt<2 * LOADS_PER_STAGE>();
-    else wait_vmcnt_for(KB > 1);
-  }
-  barrier();
-  Frags f;
-  Scales sc;
-  if (group0) {
-    read_frags(smem, fp, f);
-    read_scales(smem, fp, sc);
-    for (int b = 0; b < KB; b++)
-      step_g0(smem + ((b + 1) % STAGES) * STAGE_BYTES, smem + (b % STAGES) * STAGE_BYTES, lp, fp,
-              lane, b, KB, f, sc, acc);
-  } else {
-    v16f part[FM][FN];
-    for (int b = 0; b < KB; b++)
-      step_g1(smem + (b % STAGES) * STAGE_BYTES, fp, b, f, sc, part, acc);
-    promote(part, sc, acc);
-  }
-
-  // ---- epilogue: lane holds row (fr) and columns 8g + 4kq + {0..3} of each fragment ----
-#pragma unroll
-  for (int mi = 0; mi < FM; mi++) {
-    const int mloc = wm * WAVE_M + mi * 32 + fr;
-    if (mloc >= rows) continue;
-    const size_t crow = (size_t)(row0 + mloc) * N;
-#pragma unroll
-    for (int ni = 0; ni < FN; ni++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = n0 + wn * WAVE_N + ni * 32 + g * 8 + kq * 4;
-        if (col < N)
-          store4<OUT>(p.C, crow + col, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
-                      acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+      for (int j = 0; j < NJ; j++) {
+        const int col = n0 + wn * WN + j * 16 + q * 4;
+        if (col < N) store4<OUT>(p.C, crow + col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
+    }
+    if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass
   }
 }
 
@@ -335,7 +310,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 
 hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream) {
   const int n_blocks = (a.N + BN - 1) / BN;
-  const long long blocks = (long long)a.num_tiles * n_blocks;
+  const long long blocks = (long long)((a.num_tiles + 1) / 2) * n_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0LL) return hipErrorInvalidValue;
   dim3 grid(grid_for(blocks)), block(NTHREADS);
