@@ -4,21 +4,34 @@
 // matrix instruction, as its async_mma_scaled_impl does with tcgen05_mma_scaled; reference
 // result A_ref @ B_ref^T of its make_problem).
 //
-// CDNA4 mapping: v_mfma_scale_f32_32x32x64_f8f6f4 takes per-lane e8m0 scales for the
-// 32-element K chunk each lane supplies, so no software promotion is needed and the fp32
-// accumulator chains through the instruction. Same block structure as the blockwise kernel:
-// 8 waves, 128 x 256 tile, 2 x 2 fragments of 32 x 32 per wave, 3-stage LDS ring filled by
-// direct global->LDS loads; per stage each row's four scale bytes (128 K) are one dword
-// staged next to the tiles. Supports the tile map (grouped) and one dense group.
+// CDNA4 mapping: v_mfma_scale_f32_16x16x128_f8f6f4 takes one e8m0 scale per lane, so the scales
+// are applied by the matrix unit, the fp32 accumulator chains through the instruction and no
+// software promotion is needed. Block structure as in the blockwise kernel: 256 x 256 block
+// tiles (super-tiles of two 128-row M-tiles of one expert), 8 waves of 64 x 128 as 4 x 8
+// fragments of 16 x 16, A fragments resident and B fragments streamed two ahead, a 2-stage LDS
+// ring filled by buffer -> LDS copies, one barrier per K block. The scales of a super-tile's
+// rows are staged 8 K blocks at a time (one dword of four scales per row and K block).
+//
+// Lane layout of one 128-wide K block (probed on gfx950): the scale of (row r, 32-K chunk c) is
+// supplied by lane 16 c + r, so lane (r16 = l % 16, q = l / 16) supplies chunk q of its row.
+// e2m1: lane (r16, q) holds chunk q itself (16 bytes, low nibble = even K). e4m3: lane (r16, q)
+// holds K [16 q, 16 q + 16) in bytes 0..15 and K [64 + 16 q, 64 + 16 q + 16) in bytes 16..31.
 #include "common.h"
 #include "launch.h"
 
 namespace bsg {
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 128;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128, TILE_M = 128;
 constexpr int NWAVES = 8, NTHREADS = NWAVES * kWave;
-constexpr int STAGES = 3;
+constexpr int WM = 64, WN = 128;                  // wave tile
+constexpr int MI = WM / 16, NJ = WN / 16;         // 4 x 8 fragments of 16 x 16
+constexpr int STAGES = 2;
+constexpr int SC_CHUNK = 8;                       // K blocks per staged scale chunk
+constexpr int SC_BYTES = BM * SC_CHUNK * 4;       // 8 KiB per operand and chunk
+constexpr int SC_INSTR = SC_BYTES / 256 / NWAVES; // 4 (4-byte copies, 64 lanes)
 
 // element format codes of the f8f6f4 instruction: 0 = e4m3, 4 = e2m1
 template <int F> struct Elem;
@@ -28,97 +41,95 @@ template <> struct Elem<2> { static constexpr int kRowBytes = 64; static constex
 template <int FA, int FB>
 struct Layout {
   static constexpr int RA = Elem<FA>::kRowBytes, RB = Elem<FB>::kRowBytes;
-  static constexpr int A_BYTES = BM * RA;
-  static constexpr int B_BYTES = BN * RB;
-  static constexpr int AS_OFF = A_BYTES + B_BYTES;              // dword of 4 scales per A row
-  static constexpr int BS_OFF = AS_OFF + BM * 4;                // dword per B row
-  static constexpr int STAGE_BYTES = BS_OFF + BN * 4;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  // 1 KiB instructions per wave per stage: A rows, B rows; plus one A-scale and one B-scale load
-  static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;
+  static constexpr int A_BYTES = BM * RA, B_BYTES = BN * RB;       // per stage
+  static constexpr int A_REGION = 0;
+  static constexpr int B_REGION = STAGES * A_BYTES;
+  static constexpr int SA_REGION = B_REGION + STAGES * B_BYTES;    // 2 chunks of A scales
+  static constexpr int SB_REGION = SA_REGION + 2 * SC_BYTES;       // 2 chunks of B scales
+  static constexpr int LDS_BYTES = SB_REGION + 2 * SC_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;          // 1 KiB copies per wave
   static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
-  static constexpr int LOADS = A_INSTR + B_INSTR + 2;
-  static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the load split");
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small for the copy split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
+// 16-byte chunk swizzle of a tile row: 128-byte rows (e4m3) use swz8; for 64-byte rows (e2m1)
+// two rows share a 128-byte bank line, and rows of one parity take the four slot permutations.
 template <int ROWB>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (ROWB == 128) return swz8(r); else return swz4(r);
+__device__ __forceinline__ int swzr(int r) {
+  if constexpr (ROWB == 128) return swz8(r); else return (r >> 1) & 3;
 }
 
-// Fragment operand for one 64-wide K half (K chunks 2kh and 2kh+1 of 32 elements each).
-// The scale supplied by lane l covers row l % 32, chunk l / 32 of the half. For e2m1 the lane
-// holds that whole chunk (16 bytes). For e4m3 the instruction takes bytes 0..15 of every lane
-// from the first chunk and bytes 16..31 from the second, lane halves kq = 0 / 1 splitting each
-// chunk: so lane kq reads K [16 kq, 16 kq + 16) of both chunks.
 template <int ROWB>
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int kh, int kq) {
+struct FragBase {
+  int off[2];   // byte offsets (inside a tile, row r16 of fragment 0) of the lane's two chunks
+};
+
+// Lane (r16, q) offsets inside a tile: e4m3 chunks q and 4 + q of the 128-byte row, e2m1 chunk q
+// of the 64-byte row. The swizzle of row 16 f + r16 depends on r16 only.
+template <int ROWB>
+__device__ __forceinline__ FragBase<ROWB> frag_base(int row, int r16, int q) {
+  FragBase<ROWB> b;
+  const int sw = swzr<ROWB>(r16);
   if constexpr (ROWB == 128) {
-    const int c0 = kh * 4 + kq, c1 = kh * 4 + 2 + kq;
-    return cat(lds_read16(tile + r * ROWB + ((c0 ^ swz8(r)) * 16)),
-               lds_read16(tile + r * ROWB + ((c1 ^ swz8(r)) * 16)));
+    b.off[0] = row * ROWB + ((q ^ sw) * 16);
+    b.off[1] = row * ROWB + (((4 + q) ^ sw) * 16);
   } else {
-    const int c = kh * 2 + kq;
-    const v4i v = lds_read16(tile + r * ROWB + ((c ^ swz4(r)) * 16));
+    b.off[0] = row * ROWB + ((q ^ sw) * 16);
+    b.off[1] = b.off[0];
+  }
+  return b;
+}
+
+template <int ROWB>
+__device__ __forceinline__ v8i read_frag(const uint8_t* p, const FragBase<ROWB>& b) {
+  if constexpr (ROWB == 128) {
+    return cat(lds_read16(p + b.off[0]), lds_read16(p + b.off[1]));
+  } else {
+    const v4i v = lds_read16(p + b.off[0]);
     return (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
   }
 }
 
 template <int FA, int FB>
 struct MxLoadPlan {
-  const uint8_t* a_src[Layout<FA, FB>::A_INSTR];
-  const uint8_t* b_src[Layout<FA, FB>::B_INSTR];
-  const uint8_t* sa_src;
-  const uint8_t* sb_src;
-  int a_dst[Layout<FA, FB>::A_INSTR], b_dst[Layout<FA, FB>::B_INSTR], sa_dst, sb_dst;
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
+  uint32_t a_voff[Layout<FA, FB>::A_INSTR], b_voff[Layout<FA, FB>::B_INSTR];
+  uint32_t sc_voff_a, sc_voff_b;   // scale chunk: lane part (row and dword inside the chunk)
+  uint32_t sc_row8_a, sc_row8_b;   // scale chunk: bytes of 8 rows of the scale tensors
+  int a_dst, b_dst;
 };
 
 template <int FA, int FB>
-__device__ __forceinline__ void mx_issue(uint8_t* dst, const MxLoadPlan<FA, FB>& lp, int kb, int lane) {
+__device__ __forceinline__ void mx_issue(uint8_t* __restrict__ da, uint8_t* __restrict__ db,
+                                         const MxLoadPlan<FA, FB>& lp, int kb) {
   using L = Layout<FA, FB>;
+  kb = __builtin_amdgcn_readfirstlane(kb);
 #pragma unroll
-  for (int i = 0; i < L::A_INSTR; i++) g2lds16(lp.a_src[i] + (size_t)kb * L::RA, as_lds(dst + lp.a_dst[i]));
+  for (int i = 0; i < L::A_INSTR; i++)
+    buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)kb * L::RA, as_lds(da + lp.a_dst + i * 1024));
 #pragma unroll
-  for (int i = 0; i < L::B_INSTR; i++) g2lds16(lp.b_src[i] + (size_t)kb * L::RB, as_lds(dst + lp.b_dst[i]));
-  if (lane < 16) g2lds4(lp.sa_src + (size_t)kb * 4, as_lds(dst + lp.sa_dst));
-  if (lane < 32) g2lds4(lp.sb_src + (size_t)kb * 4, as_lds(dst + lp.sb_dst));
+  for (int i = 0; i < L::B_INSTR; i++)
+    buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)kb * L::RB, as_lds(db + lp.b_dst + i * 1024));
 }
 
-// One K block of 128: copies of K block kb_next into `nxt` (if requested), then four pairs of
-// scaled MFMAs on the operands in `cur`. The two stages are distinct (see the blockwise kernel).
+// Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows into
+// [row][8 dwords] layouts; wave w copies rows 32 w .. 32 w + 31 of each.
 template <int FA, int FB>
-__device__ __forceinline__ void mx_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt,
-                                        const MxLoadPlan<FA, FB>& lp, bool issue, int kb_next,
-                                        int lane, int wm, int wn, v16f (&acc)[2][2]) {
-  using L = Layout<FA, FB>;
-  if (issue) mx_issue<FA, FB>(nxt, lp, kb_next, lane);
-  const int fr = lane & 31, kq = lane >> 5;
-  v8i af[2][2], bf[2][2];
-  int sa[2], sb[2];
+__device__ __forceinline__ void mx_issue_scales(uint8_t* __restrict__ dsa, uint8_t* __restrict__ dsb,
+                                                const MxLoadPlan<FA, FB>& lp, int chunk, int wave) {
+  const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * SC_CHUNK * 4;
 #pragma unroll
-  for (int f = 0; f < 2; f++) {
-    const int ra = wm * 64 + f * 32 + fr, rb = wn * 64 + f * 32 + fr;
-#pragma unroll
-    for (int kh = 0; kh < 2; kh++) {
-      af[f][kh] = read_frag<L::RA>(cur, ra, kh, kq);
-      bf[f][kh] = read_frag<L::RB>(cur + L::A_BYTES, rb, kh, kq);
-    }
-    // byte j of the row's dword is the scale of K chunk j (32 elements); lanes of the upper
-    // half supply chunks 1 and 3, so their dword is shifted by one byte and bytes 0 / 2 are
-    // selected for the two K halves.
-    sa[f] = (int)(*(const uint32_t*)(cur + L::AS_OFF + ra * 4) >> (8 * kq));
-    sb[f] = (int)(*(const uint32_t*)(cur + L::BS_OFF + rb * 4) >> (8 * kq));
+  for (int i = 0; i < SC_INSTR; i++) {
+    buf2lds4(lp.sa_rsrc, lp.sc_voff_a + col + i * lp.sc_row8_a, 0, as_lds(dsa + (wave * SC_INSTR + i) * 256));
+    buf2lds4(lp.sb_rsrc, lp.sc_voff_b + col + i * lp.sc_row8_b, 0, as_lds(dsb + (wave * SC_INSTR + i) * 256));
   }
-#pragma unroll
-  for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-    for (int ni = 0; ni < 2; ni++) {
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          bf[ni][0], af[mi][0], acc[mi][ni], Elem<FB>::kCode, Elem<FA>::kCode, 0, sb[ni], 0, sa[mi]);
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          bf[ni][1], af[mi][1], acc[mi][ni], Elem<FB>::kCode, Elem<FA>::kCode, 2, sb[ni], 2, sa[mi]);
-    }
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ v4f mma(const v8i& b, const v8i& a, const v4f& c, int sb, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, Elem<FB>::kCode, Elem<FA>::kCode,
+                                                          0, sb, 0, sa);
 }
 
 template <int FA, int FB, int OUT>
@@ -128,80 +139,180 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int t, nb;
-  if (!work_item(p.num_tiles, n_blocks, 8, t, nb)) return;
-  const int n0 = nb * BN;
-  const TileRows tr = tile_rows(p.expert_ids, p.tile_offsets, t, p.M, BM, p.num_experts);
-  if (tr.rows <= 0) return;
-  const int e = tr.expert, row0 = tr.row0, rows = tr.rows;
-  const int N = p.N, KB = p.K / BK;
-  const size_t K = (size_t)p.K;
-  const size_t rowA = K * L::RA / BK, rowB = K * L::RB / BK;   // bytes per full row
-  const size_t srow = K / 32;                                   // scale bytes per row
-  const uint8_t* A = (const uint8_t*)p.A;
-  const uint8_t* Be = (const uint8_t*)p.B + (size_t)e * N * rowB;
-  const uint8_t* SA = (const uint8_t*)p.a_scales;
-  const uint8_t* SBe = (const uint8_t*)p.b_scales + (size_t)e * N * srow;
+  const int num_super = (p.num_tiles + 1) / 2;
+  int s, nb;
+  if (!work_item(num_super, n_blocks, 8, s, nb)) return;
+  const int n0 = nb * BN, N = p.N, KB = p.K / BK;
+  const size_t rowA = (size_t)p.K * L::RA / BK, rowB = (size_t)p.K * L::RB / BK;   // bytes per row
+  const size_t srow = (size_t)p.K / 32;                                            // scale bytes per row
+  const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
+  const int r16 = lane & 15, q = lane >> 4;
+  const int ncols = min(BN, N - n0);
 
-  // ---- load plan: a 1 KiB instruction covers 1024 / rowbytes rows ----
-  constexpr int CA = L::RA / 16, CB = L::RB / 16;              // chunks per LDS row
-  MxLoadPlan<FA, FB> lp;
-#pragma unroll
-  for (int i = 0; i < L::A_INSTR; i++) {
-    const int first = (wave * L::A_INSTR + i) * (1024 / L::RA);
-    const int r = first + lane / CA, slot = lane % CA;
-    const int gr = row0 + min(r, rows - 1);
-    lp.a_src[i] = A + (size_t)gr * rowA + (size_t)((slot ^ swz<L::RA>(r)) * 16);
-    lp.a_dst[i] = first * L::RA;
-  }
-#pragma unroll
-  for (int i = 0; i < L::B_INSTR; i++) {
-    const int first = (wave * L::B_INSTR + i) * (1024 / L::RB);
-    const int r = first + lane / CB, slot = lane % CB;
-    const int gn = min(n0 + r, N - 1);
-    lp.b_src[i] = Be + (size_t)gn * rowB + (size_t)((slot ^ swz<L::RB>(r)) * 16);
-    lp.b_dst[i] = L::A_BYTES + first * L::RB;
-  }
-  // scales: wave w stages A rows 16w + (lane & 15) and B rows 32w + (lane & 31)
-  lp.sa_src = SA + (size_t)(row0 + min(wave * 16 + (lane & 15), rows - 1)) * srow;
-  lp.sb_src = SBe + (size_t)min(n0 + wave * 32 + (lane & 31), N - 1) * srow;
-  lp.sa_dst = L::AS_OFF + wave * 16 * 4;
-  lp.sb_dst = L::BS_OFF + wave * 32 * 4;
-
-  const int wm = wave & 1, wn = wave >> 1;
-  const int fr = lane & 31, kq = lane >> 5;
-
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = (v16f){};
-
-  mx_issue<FA, FB>(smem, lp, 0, lane);
-  if (KB > 1) mx_issue<FA, FB>(smem + L::STAGE_BYTES, lp, 1, lane);
-
-  for (int kb = 0; kb < KB; kb++) {
-    const int s = kb % STAGES, s2 = (kb + 2) % STAGES;
-    if (kb + 1 < KB) wait_vmcnt<L::LOADS>(); else wait_vmcnt<0>();
-    barrier();                                                 // stage s landed; stage s2 free
-    mx_step<FA, FB>(smem + s * L::STAGE_BYTES, smem + s2 * L::STAGE_BYTES, lp, kb + 2 < KB, kb + 2,
-                    lane, wm, wn, acc);
+  // the super-tile's passes, as in the blockwise kernel
+  const TileRows t0 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s, p.M, TILE_M, p.num_experts);
+  TileRows t1 = {0, 0, 0};
+  if (2 * s + 1 < p.num_tiles)
+    t1 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s + 1, p.M, TILE_M, p.num_experts);
+  int e0 = t0.expert, r0 = t0.row0, n0rows = t0.rows, e1 = t1.expert, r1 = t1.row0, n1rows = t1.rows;
+  int npass;
+  if (t0.rows == TILE_M && t1.rows > 0 && t1.expert == t0.expert && t1.row0 == t0.row0 + TILE_M) {
+    n0rows = TILE_M + t1.rows;
+    npass = 1;
+  } else if (t0.rows > 0) {
+    npass = t1.rows > 0 ? 2 : 1;
+  } else {
+    e0 = e1; r0 = r1; n0rows = n1rows;
+    npass = t1.rows > 0 ? 1 : 0;
   }
 
+  const FragBase<L::RA> fa = frag_base<L::RA>(wm * WM + r16, r16, q);
+  const FragBase<L::RB> fb = frag_base<L::RB>(wn * WN + r16, r16, q);
+  const int base_sa = L::SA_REGION + (wm * WM + r16) * SC_CHUNK * 4;
+  const int base_sb = L::SB_REGION + (wn * WN + r16) * SC_CHUNK * 4;
+
+  for (int ps = 0; ps < npass; ps++) {
+    const int e = __builtin_amdgcn_readfirstlane(ps == 0 ? e0 : e1);
+    const int row0 = __builtin_amdgcn_readfirstlane(ps == 0 ? r0 : r1);
+    const int rows = __builtin_amdgcn_readfirstlane(ps == 0 ? n0rows : n1rows);
+
+    // Copy plan. Every row offset is in the per-lane offset, which the resource bounds check:
+    // rows past the pass or past N read as zero.
+    MxLoadPlan<FA, FB> lp;
+    lp.a_rsrc = make_rsrc((const uint8_t*)p.A + (size_t)row0 * rowA, (uint64_t)rows * rowA);
+    lp.b_rsrc = make_rsrc((const uint8_t*)p.B + ((size_t)e * N + n0) * rowB, (uint64_t)ncols * rowB);
+    lp.sa_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)row0 * srow, (uint64_t)rows * srow);
+    lp.sb_rsrc = make_rsrc((const uint8_t*)p.b_scales + ((size_t)e * N + n0) * srow, (uint64_t)ncols * srow);
+    {
+      constexpr int CA = L::RA / 16, CB = L::RB / 16;            // 16-byte chunks per tile row
+      constexpr int PA = 1024 / L::RA, PB = 1024 / L::RB;        // tile rows per 1 KiB copy
 #pragma unroll
-  for (int mi = 0; mi < 2; mi++) {
-    const int mloc = wm * 64 + mi * 32 + fr;
-    if (mloc >= rows) continue;
-    const size_t crow = (size_t)(row0 + mloc) * N;
-#pragma unroll
-    for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int col = n0 + wn * 64 + ni * 32 + g * 8 + kq * 4;
-        if (col < N)
-          store4<OUT>(p.C, crow + col, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
-                      acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+      for (int i = 0; i < L::A_INSTR; i++) {
+        const int r = (wave * L::A_INSTR + i) * PA + lane / CA, slot = lane % CA;
+        lp.a_voff[i] = (uint32_t)(r * rowA + ((slot ^ swzr<L::RA>(r)) * 16));
       }
+#pragma unroll
+      for (int i = 0; i < L::B_INSTR; i++) {
+        const int r = (wave * L::B_INSTR + i) * PB + lane / CB, slot = lane % CB;
+        lp.b_voff[i] = (uint32_t)(r * rowB + ((slot ^ swzr<L::RB>(r)) * 16));
+      }
+      lp.a_dst = wave * L::A_INSTR * 1024;
+      lp.b_dst = wave * L::B_INSTR * 1024;
+      const int lrow = lane >> 3, dw = lane & 7;                 // scale chunk: 8 rows x 8 dwords
+      lp.sc_voff_a = (uint32_t)((wave * 32 + lrow) * srow + dw * 4);
+      lp.sc_voff_b = lp.sc_voff_a;
+      lp.sc_row8_a = lp.sc_row8_b = (uint32_t)(8 * srow);
+    }
+
+    v4f acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+      for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // prologue: scale chunks 0 and 1, blocks 0 and 1 in flight; block 0 published
+    mx_issue_scales<FA, FB>(smem + L::SA_REGION, smem + L::SB_REGION, lp, 0, wave);
+    mx_issue_scales<FA, FB>(smem + L::SA_REGION + SC_BYTES, smem + L::SB_REGION + SC_BYTES, lp, 1, wave);
+    mx_issue<FA, FB>(smem + L::A_REGION, smem + L::B_REGION, lp, 0);
+    mx_issue<FA, FB>(smem + L::A_REGION + L::A_BYTES, smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1));
+    wait_vmcnt<0>();
+    barrier();
+
+    // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, moved to byte 0
+    auto scale_a = [&](int kb, int i) {
+      const int so = ((kb / SC_CHUNK) & 1) * SC_BYTES + (kb % SC_CHUNK) * 4;
+      return (int)(*(const uint32_t*)(smem + base_sa + so + i * 16 * SC_CHUNK * 4) >> (8 * q));
+    };
+    auto scale_b = [&](int kb, int j) {
+      const int so = ((kb / SC_CHUNK) & 1) * SC_BYTES + (kb % SC_CHUNK) * 4;
+      return (int)(*(const uint32_t*)(smem + base_sb + so + j * 16 * SC_CHUNK * 4) >> (8 * q));
+    };
+
+    // A fragments and scales of the block stay in registers; B fragments and their scales
+    // stream through 3-deep queues two fragments ahead
+    v8i af[MI], bq[3];
+    int sa[MI], sbq[3];
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+      af[i] = read_frag<L::RA>(smem + L::A_REGION + i * 16 * L::RA, fa);
+      sa[i] = scale_a(0, i);
+    }
+    bq[0] = read_frag<L::RB>(smem + L::B_REGION, fb);
+    bq[1] = read_frag<L::RB>(smem + L::B_REGION + 16 * L::RB, fb);
+    sbq[0] = scale_b(0, 0);
+    sbq[1] = scale_b(0, 1);
+
+    for (int b = 0; b < KB; b++) {
+      const int S = b & 1;
+      const int soa = S * L::A_BYTES, sob = S * L::B_BYTES;                 // this block's stage
+      const int sna = (S ^ 1) * L::A_BYTES, snb = (S ^ 1) * L::B_BYTES;
+      const int bn = min(b + 1, KB - 1);
+      // passes 0..6: B fragment j against the 4 resident A fragments; B fragment j + 2 and its
+      // scale are read at the start of pass j
+#pragma unroll
+      for (int j = 0; j < NJ - 1; j++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 2 < NJ) {
+          bq[(j + 2) % 3] = read_frag<L::RB>(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB, fb);
+          sbq[(j + 2) % 3] = scale_b(b, j + 2);
+        }
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+          acc[i][j] = mma<FA, FB>(bq[j % 3], af[i], acc[i][j], sbq[j % 3], sa[i]);
+        // pin the previous pass's MFMAs (complete by now) ahead of this point, so that the
+        // compiler does not sink them past the loop's branch
+        if (j > 0) {
+#pragma unroll
+          for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][j - 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // stage S fully read, block b+1 landed: publish it, then refill stage S
+      wait_vmcnt<0>();
+      wait_lds_reads();
+      barrier();
+      // scales of chunk c+1 replace those of chunk c-1 while block 8c is computed
+      if (b % SC_CHUNK == 0 && b > 0) {
+        const int cb = ((b / SC_CHUNK + 1) & 1) * SC_BYTES;
+        mx_issue_scales<FA, FB>(smem + L::SA_REGION + cb, smem + L::SB_REGION + cb, lp, b / SC_CHUNK + 1, wave);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
+      __builtin_amdgcn_sched_barrier(0);
+      // pass 7: last B fragment; each A fragment and its scale are refilled from block b+1
+      // right after their MFMA; the first two B fragments of block b+1 and their scales are
+      // read; copies of block b+2 into stage S (past the last block they repeat block KB-1
+      // into a stage not read again)
+#pragma unroll
+      for (int i = 0; i < MI; i++) {
+        acc[i][NJ - 1] = mma<FA, FB>(bq[(NJ - 1) % 3], af[i], acc[i][NJ - 1], sbq[(NJ - 1) % 3], sa[i]);
+        af[i] = read_frag<L::RA>(smem + L::A_REGION + sna + i * 16 * L::RA, fa);
+        sa[i] = scale_a(bn, i);
+      }
+      bq[0] = read_frag<L::RB>(smem + L::B_REGION + snb, fb);
+      bq[1] = read_frag<L::RB>(smem + L::B_REGION + snb + 16 * L::RB, fb);
+      sbq[0] = scale_b(bn, 0);
+      sbq[1] = scale_b(bn, 1);
+      mx_issue<FA, FB>(smem + L::A_REGION + soa, smem + L::B_REGION + sob, lp, min(b + 2, KB - 1));
+#pragma unroll
+      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();
+
+    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N fragment
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+      const int mloc = wm * WM + i * 16 + r16;
+      if (mloc >= rows) continue;
+      const size_t crow = (size_t)(row0 + mloc) * N;
+#pragma unroll
+      for (int j = 0; j < NJ; j++) {
+        const int col = n0 + wn * WN + j * 16 + q * 4;
+        if (col < N) store4<OUT>(p.C, crow + col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+    if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass
   }
 }
 
@@ -221,7 +332,7 @@ hipError_t launch_fmt(const GemmArgs& a, int out, hipStream_t stream, dim3 grid,
 
 hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream) {
   const int n_blocks = (a.N + BN - 1) / BN;
-  const long long blocks = (long long)a.num_tiles * n_blocks;
+  const long long blocks = (long long)((a.num_tiles + 1) / 2) * n_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0LL) return hipErrorInvalidValue;
   const dim3 grid(grid_for(blocks));
