@@ -12,7 +12,11 @@ step time. The JSON line also carries the roofline of the dominant kernel (gate_
 per-launch time is measured with HIP events on the stream the kernels run on, and the CPU
 oracle's rate on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+With --workload mx8192_<a>_<b> a step is instead one dense MX GEMM of 8192^3 (e8m0 scales per
+32 K, fp16 out) with formats a x b; its roofline is that launch against the peak of the
+narrower-rate format pair.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload W]
        python bench.py --copy-calibration MIB --steps K   (HBM counter calibration)
 """
 
@@ -29,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5033.0   # MI355X dense FP8 MFMA peak (256 CU x 2.4 GHz x 8192 flop/clk)
+PEAK_FP4_TFLOPS = 10066.0  # MI355X dense MXFP4 MFMA peak (twice the FP8 rate)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 
@@ -52,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="moe32",
+                    choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB "
                          "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
@@ -88,6 +95,78 @@ def cpu_baseline(problems, n_experts=16, rows_per_expert=128):
     }
 
 
+def cpu_baseline_mx(p, rows=1024):
+    """Time the oracle on the first ``rows`` rows of A of the MX GEMM (all N, all K)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as og
+
+    qa, sa = p.qa[:rows].cpu().numpy(), p.a_scales[:rows].cpu().numpy()
+    qb, sb = p.qb.cpu().numpy(), p.b_scales.cpu().numpy()
+    t0 = time.perf_counter()
+    og.mx_gemm(qa, sa, qb, sb, p.fmt_a, p.fmt_b)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": 2.0 * rows * p.N * p.K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows} rows of A of the {p.M}x{p.N}x{p.K} MX GEMM ({p.fmt_a} x {p.fmt_b}), "
+                  f"fp64 oracle (decode, then one product); {dt:.1f} s",
+    }
+
+
+def bench_mx(args, torch, bsg, make_problem):
+    """A step is one dense MX GEMM launch on a resident 8192^3 problem."""
+    p = make_problem(args.workload, device="cuda", seed=args.seed)
+    C = torch.empty(p.M, p.N, dtype=torch.float16, device="cuda")
+    fmt = bsg.make_fmt(p.fmt_a, p.fmt_b, "mx", "f16")
+    stream = torch.cuda.current_stream()
+    launches = []
+
+    def step(record):
+        a = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            a.record(stream)
+        bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C, p.M, p.N, p.K, fmt,
+                           num_tiles=p.M // 128, num_experts=1, stream=stream)
+        if record:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            launches.append((a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in launches]))
+    flops = p.useful_flops
+    peak = PEAK_FP4_TFLOPS if (p.fmt_a, p.fmt_b) == ("e2m1", "e2m1") else PEAK_FP8_TFLOPS
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": f"TFLOP/s, MX GEMM {p.M}x{p.N}x{p.K} ({p.fmt_a} x {p.fmt_b}, e8m0 per 32)",
+        "value": round(value, 2), "unit": "TFLOP/s", "pct_of_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"{p.fmt_a}x{p.fmt_b}", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: dense MX GEMM M=N=K=8192, e8m0 scales per 32 K, "
+                               f"fp16 out", "seed": args.seed},
+        "kernels_ms": {"mx": round(kernel_ms, 4)},
+        "roofline": {
+            "kernel": f"mx_kernel<{p.fmt_a}, {p.fmt_b}>", "bound": "mfma",
+            "achieved": round(kernel_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(kernel_tflops / peak, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mx(p)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +195,10 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     bsg.load_library()
+
+    if args.workload != "moe32":
+        bench_mx(args, torch, bsg, make_problem)
+        return
 
     problems = {
         "gate_up": make_problem("moe32_gate_up_n4096_k7168", device="cuda", seed=args.seed),
