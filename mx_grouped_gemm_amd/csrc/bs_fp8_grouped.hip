@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int num_super = (p.num_tiles + 1) / 2;
   int s, nb;
-  if (!work_item(num_super, n_blocks, 8, s, nb)) return;
+  if (!work_item(num_super, n_blocks, 1, s, nb)) return;
   const int n0 = nb * BN, N = p.N, KB = p.K / BK;
   const size_t K = (size_t)p.K;
   const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
