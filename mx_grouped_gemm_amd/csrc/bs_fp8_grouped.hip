@@ -20,9 +20,9 @@
 //    fragments stream through a 3-deep register queue two fragments ahead of their MFMAs.
 //  * operands stream through a 2-stage LDS ring filled by buffer -> LDS copies
 //    (buffer_load_dwordx4 ... lds); 16-byte chunks are XOR-swizzled so fragment reads are free
-//    of bank conflicts. One barrier per K block, after the last read of the block's stage: the
-//    copies of block b+2 then refill that stage while the last B fragment's MFMAs run and the
-//    A fragments of block b+1 are read.
+//    of bank conflicts. One barrier per K block, after the last read of the block's stage (in
+//    pass 5 of 8): the copies of block b+2 then refill that stage while the last two B
+//    fragments' MFMAs run and the A fragments of block b+1 are read.
 //  * A scales: each tile's rows are staged 8 K blocks at a time (256 rows x 8 floats, double
 //    buffered), so a 128-byte line of the row-major a_scales serves 8 K blocks instead of one.
 //    The B scale of each of the two 128-column blocks rides in the stage.
@@ -208,13 +208,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int i = 0; i < MI; i++) sc[i] = as_raw[i] * bs_raw;
       v4f part[3];
-      // passes 0..6: B fragment j against the 4 resident A fragments; B fragment j + 2 is read
-      // at the start of pass j. The promotion of each partial is pinned right after the MFMA two
-      // slots later, which also keeps the MFMAs in their pass.
+      // passes 0..5: B fragment j against the 4 resident A fragments, at raised wave priority so
+      // the SIMD's arbiter favours feeding the matrix unit; B fragment j + 2 is read in two
+      // halves, after the first and the third MFMA. The promotion of each partial is pinned
+      // right after the MFMA two slots later, which also keeps the MFMAs in their pass.
 #pragma unroll
-      for (int j = 0; j < NJ - 1; j++) {
+      for (int j = 0; j < NJ - 2; j++) {
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 2 < NJ) bq[(j + 2) % 3] = read_frag(smem + so_ab + (j + 2) * 2048, base_b);
+        v4i lo, hi;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < MI; i++) {
           const int k = j * MI + i;
@@ -224,12 +226,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
             acc[ip][jp] += part[kp % 3] * sc[ip];
             asm volatile("" : "+v"(acc[ip][jp]));
           }
+          if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[0]);
+          if (j + 2 < NJ && i == 2) hi = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[1]);
         }
-        if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_s_setprio(0);
+        if (j + 2 < NJ) bq[(j + 2) % 3] = cat(lo, hi);
 #pragma unroll
         for (int i = 0; i < MI; i++) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          if ((i & 1) == 0 && j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -239,10 +245,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       wait_lds_reads();
       barrier();
       __builtin_amdgcn_sched_barrier(0);
+      // pass 6 (B fragment 6, no reads left in this block) with the copies of block b+2 into
+      // stage S (past the last block they repeat block KB-1 into a stage that is not read again)
+#pragma unroll
+      for (int i = 0; i < MI; i++) {
+        const int k = (NJ - 2) * MI + i;
+        part[k % 3] = mma(bq[(NJ - 2) % 3], af[i]);
+        const int kp = k - 2, jp = kp / MI, ip = kp % MI;
+        acc[ip][jp] += part[kp % 3] * sc[ip];
+        asm volatile("" : "+v"(acc[ip][jp]));
+      }
+      issue_stage(smem + A_REGION + so_ab, smem + B_REGION + so_ab, smem + BS_REGION + so_bs, lp,
+                  min(b + 2, KB - 1), wave);
+      if (b % AS_CHUNK == 0 && b > 0)
+        issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
+                          wave);
+#pragma unroll
+      for (int i = 0; i < MI; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 2);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
-      // MFMA, then the first two B fragments and the scales of block b+1 are read and the copies
-      // of block b+2 go into stage S (past the last block they repeat block KB-1 into a stage
-      // that is not read again).
+      // MFMA, then the first two B fragments and the scales of block b+1 are read.
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 1) * MI + i;
@@ -264,19 +290,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           as_raw[i] = *(const float*)(smem + base_as + as_off + i * 16 * AS_CHUNK * 4);
       }
       bs_raw = *(const float*)(smem + sn_bs + base_bs);
-      issue_stage(smem + A_REGION + so_ab, smem + B_REGION + so_ab, smem + BS_REGION + so_bs, lp,
-                  min(b + 2, KB - 1), wave);
-      // The A scales of chunk c+1 (blocks 8c+8..) replace those of chunk c-1 while block 8c is
-      // computed: chunk c-1 was last read for block 8c-1.
-      if (b % AS_CHUNK == 0 && b > 0)
-        issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
-                          wave);
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the last two partials of the block
