@@ -21,10 +21,14 @@
 //  * operands stream through a 2-stage LDS ring filled by buffer -> LDS copies
 //    (buffer_load_dwordx4 ... lds); 16-byte chunks are XOR-swizzled so fragment reads are free
 //    of bank conflicts. One barrier per K block, after the last read of the block's stage (in
-//    pass 5 of 8): the copies of block b+2 then refill that stage while the last two B
-//    fragments' MFMAs run and the A fragments of block b+1 are read.
+//    pass 5 of 8) frees that stage for block b+2. A wave that issues a copy can stall at issue
+//    while the CU's address unit works through the other waves' copies, so the 8 copies per
+//    wave go out two per pass, each after an MFMA: B in passes 6 and 7 of block b, A (and the
+//    B scales) in passes 0 and 1 of block b+1, all landing before the barrier of block b+1.
 //  * A scales: each tile's rows are staged 8 K blocks at a time (256 rows x 8 floats, double
 //    buffered), so a 128-byte line of the row-major a_scales serves 8 K blocks instead of one.
+//    Column c of row r sits at slot c ^ ((r >> 3) & 7): the 16 rows one read instruction touches
+//    (and the 4 rows of one lane) then fall in distinct banks.
 //    The B scale of each of the two 128-column blocks rides in the stage.
 //  * the MFMA computes C^T fragments (B rows as the first operand) so that each lane holds 4
 //    consecutive output columns of one row: the epilogue writes 8-byte (bf16/fp16) or 16-byte
@@ -58,33 +62,35 @@ constexpr int AS_INSTR = AS_BYTES / 256 / NWAVES;            // 4 (4-byte copies
 struct LoadPlan {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, bs_rsrc, as_rsrc;
   uint32_t voff[A_INSTR];  // data copies: per-lane offset of instruction i (same for A and B)
-  uint32_t as_voff;      // A scale chunk: lane part (row and column inside the chunk)
+  uint32_t as_vrow;      // A scale chunk: lane part of the row offset
   uint32_t as_row8;      // A scale chunk: bytes of 8 rows of a_scales
   int a_dst, b_dst;
 };
 
-// Copies of K block kb into one stage; every AS_CHUNK-th call also stages the A scales of the
-// chunk that starts AS_CHUNK blocks later.
-__device__ __forceinline__ void issue_stage(uint8_t* __restrict__ da, uint8_t* __restrict__ db,
-                                            uint8_t* __restrict__ dbs, const LoadPlan& lp, int kb,
-                                            int wave) {
-  kb = __builtin_amdgcn_readfirstlane(kb);
-  const uint32_t koff = (uint32_t)kb * BK;
-#pragma unroll
-  for (int i = 0; i < A_INSTR; i++)
-    buf2lds16(lp.a_rsrc, lp.voff[i], koff, as_lds(da + lp.a_dst + i * 1024));
-#pragma unroll
-  for (int i = 0; i < B_INSTR; i++)
-    buf2lds16(lp.b_rsrc, lp.voff[i], koff, as_lds(db + lp.b_dst + i * 1024));
-  if (wave < 2) buf2lds4(lp.bs_rsrc, 0, (uint32_t)kb * 4, as_lds(dbs + wave * 256));
+// Copy i (of A_INSTR / B_INSTR per wave) of K block kb into the A or B half of a stage, and the
+// B scales of kb (waves 0 and 1, one column block each).
+__device__ __forceinline__ void copy_a(uint8_t* __restrict__ da, const LoadPlan& lp, int kb, int i) {
+  buf2lds16(lp.a_rsrc, lp.voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
+            as_lds(da + lp.a_dst + i * 1024));
+}
+__device__ __forceinline__ void copy_b(uint8_t* __restrict__ db, const LoadPlan& lp, int kb, int i) {
+  buf2lds16(lp.b_rsrc, lp.voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
+            as_lds(db + lp.b_dst + i * 1024));
+}
+__device__ __forceinline__ void copy_bs(uint8_t* __restrict__ dbs, const LoadPlan& lp, int kb, int wave) {
+  if (wave < 2)
+    buf2lds4(lp.bs_rsrc, 0, (uint32_t)__builtin_amdgcn_readfirstlane(kb) * 4, as_lds(dbs + wave * 256));
 }
 
 __device__ __forceinline__ void issue_scale_chunk(uint8_t* __restrict__ dst, const LoadPlan& lp,
                                                   int chunk, int wave) {
   const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * AS_CHUNK * 4;
+  const uint32_t slot = threadIdx.x & 7;
+  // instruction i of wave w fills rows 32 w + 8 i + (lane >> 3); slot (lane & 7) of such a row
+  // holds column slot ^ ((4 w + i) & 7)
 #pragma unroll
   for (int i = 0; i < AS_INSTR; i++)
-    buf2lds4(lp.as_rsrc, lp.as_voff + col + i * lp.as_row8, 0,
+    buf2lds4(lp.as_rsrc, lp.as_vrow + i * lp.as_row8 + col + ((slot ^ ((4 * wave + i) & 7)) << 2), 0,
              as_lds(dst + (wave * AS_INSTR + i) * 256));
 }
 
@@ -141,7 +147,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     base_a[h] = A_REGION + (wm * WM + r16) * BK + chunk;
     base_b[h] = B_REGION + (wn * WN + r16) * BK + chunk;
   }
-  const int base_as = AS_REGION + (wm * WM + r16) * AS_CHUNK * 4;
+  // A scale of row wm*64 + 16 i + r16, K block kb of a chunk: slot kb ^ (2 i + (r16 >> 3))
+  static_assert(AS_REGION % 32 == 0, "scale rows must be 32-byte aligned");
+  const int base_as = (AS_REGION + (wm * WM + r16) * AS_CHUNK * 4) | ((r16 >> 3) << 2);
   const int base_bs = BS_REGION + wn * 256;
 
   for (int ps = 0; ps < npass; ps++) {
@@ -170,8 +178,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
         lp.voff[i] = (uint32_t)((wave * 32 + i * 8 + lrow) * K + ((slot ^ lrow ^ (i & 1)) * 16));
       lp.a_dst = wave * A_INSTR * 1024;
       lp.b_dst = wave * B_INSTR * 1024;
-      // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow, column slot
-      lp.as_voff = (uint32_t)(((wave * 32 + lrow) * KB + slot) * 4);
+      // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow
+      lp.as_vrow = (uint32_t)((wave * 32 + lrow) * KB * 4);
       lp.as_row8 = (uint32_t)(8 * KB * 4);
     }
 
@@ -181,12 +189,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: A scales of chunks 0 and 1, blocks 0 and 1 in flight; block 0 published
+    // prologue: A scales of chunks 0 and 1, block 0 and the B half of block 1 (its A half and B
+    // scales go out in passes 0 and 1 of block 0, as in every block); block 0 published
     issue_scale_chunk(smem + AS_REGION, lp, 0, wave);
     issue_scale_chunk(smem + AS_REGION + AS_BYTES, lp, 1, wave);
-    issue_stage(smem + A_REGION, smem + B_REGION, smem + BS_REGION, lp, 0, wave);
-    issue_stage(smem + A_REGION + A_BYTES, smem + B_REGION + B_BYTES, smem + BS_REGION + BS_BYTES,
-                lp, min(1, KB - 1), wave);
+#pragma unroll
+    for (int i = 0; i < A_INSTR; i++) copy_a(smem + A_REGION, lp, 0, i);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; i++) copy_b(smem + B_REGION, lp, 0, i);
+    copy_bs(smem + BS_REGION, lp, 0, wave);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; i++) copy_b(smem + B_REGION + B_BYTES, lp, min(1, KB - 1), i);
     wait_vmcnt<0>();
     barrier();
 
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     bq[0] = read_frag(smem, base_b);
     bq[1] = read_frag(smem + 2048, base_b);
 #pragma unroll
-    for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + base_as + i * 16 * AS_CHUNK * 4);
+    for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + (base_as ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
     bs_raw = *(const float*)(smem + base_bs);
 
     for (int b = 0; b < KB; b++) {
@@ -211,7 +224,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       // passes 0..5: B fragment j against the 4 resident A fragments, at raised wave priority so
       // the SIMD's arbiter favours feeding the matrix unit; B fragment j + 2 is read in two
       // halves, after the first and the third MFMA. The promotion of each partial is pinned
-      // right after the MFMA two slots later, which also keeps the MFMAs in their pass.
+      // right after the MFMA two slots later, which also keeps the MFMAs in their pass. Passes 0
+      // and 1 also copy the A half and B scales of block b+1 into the other stage (freed by the
+      // barrier of block b-1; its B half went out in passes 6 and 7 of block b-1).
 #pragma unroll
       for (int j = 0; j < NJ - 2; j++) {
         __builtin_amdgcn_sched_barrier(0);
@@ -226,6 +241,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
             acc[ip][jp] += part[kp % 3] * sc[ip];
             asm volatile("" : "+v"(acc[ip][jp]));
           }
+          if (j < 2 && (i & 1)) {
+            copy_a(smem + A_REGION + sn_ab, lp, min(b + 1, KB - 1), 2 * j + (i >> 1));
+            if (j == 1 && i == 3) copy_bs(smem + BS_REGION + sn_bs, lp, min(b + 1, KB - 1), wave);
+          }
           if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[0]);
           if (j + 2 < NJ && i == 2) hi = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[1]);
         }
@@ -236,6 +255,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
           if ((i & 1) == 0 && j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if ((i & 1) == 1 && j < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (i == 3 && j == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -245,8 +266,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       wait_lds_reads();
       barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // pass 6 (B fragment 6, no reads left in this block) with the copies of block b+2 into
-      // stage S (past the last block they repeat block KB-1 into a stage that is not read again)
+      // pass 6 (B fragment 6, no reads left in this block) with copies 0 and 1 of the B half of
+      // block b+2 into stage S (past the last block, copies repeat block KB-1 into a stage that is
+      // not read again)
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 2) * MI + i;
@@ -254,9 +276,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
         const int kp = k - 2, jp = kp / MI, ip = kp % MI;
         acc[ip][jp] += part[kp % 3] * sc[ip];
         asm volatile("" : "+v"(acc[ip][jp]));
+        if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), i >> 1);
       }
-      issue_stage(smem + A_REGION + so_ab, smem + B_REGION + so_ab, smem + BS_REGION + so_bs, lp,
-                  min(b + 2, KB - 1), wave);
       if (b % AS_CHUNK == 0 && b > 0)
         issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
                           wave);
@@ -264,11 +285,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       for (int i = 0; i < MI; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 2);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 2);
+        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);
       }
       __builtin_amdgcn_sched_barrier(0);
       // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
-      // MFMA, then the first two B fragments and the scales of block b+1 are read.
+      // MFMA, then the first two B fragments and the scales of block b+1 are read; copies 2 and 3
+      // of the B half of block b+2.
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 1) * MI + i;
@@ -279,15 +301,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           asm volatile("" : "+v"(acc[ip][jp]));
         }
         af[i] = read_frag(smem + sn_ab + i * 2048, base_a);
+        if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), 2 + (i >> 1));
       }
       bq[0] = read_frag(smem + sn_ab, base_b);
       bq[1] = read_frag(smem + sn_ab + 2048, base_b);
       {
         const int bn = min(b + 1, KB - 1);
-        const int as_off = ((bn / AS_CHUNK) & 1) * AS_BYTES + (bn % AS_CHUNK) * 4;
+        const int as_v = (base_as ^ ((bn % AS_CHUNK) * 4)) + ((bn / AS_CHUNK) & 1) * AS_BYTES;
 #pragma unroll
         for (int i = 0; i < MI; i++)
-          as_raw[i] = *(const float*)(smem + base_as + as_off + i * 16 * AS_CHUNK * 4);
+          as_raw[i] = *(const float*)(smem + (as_v ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
       }
       bs_raw = *(const float*)(smem + sn_bs + base_bs);
 #pragma unroll
@@ -295,6 +318,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the last two partials of the block
