@@ -11,12 +11,15 @@
 // CDNA4 mapping (not the pages' Blackwell design):
 //  * block tile 256 (M) x 256 (N): two consecutive 128-row M-tiles of one expert (a lone tile,
 //    or a pair whose experts differ, runs as one or two 128-row passes). The copy traffic per
-//    flop of a 256 x 256 tile is two thirds of a 128 x 256 one; the L2 -> LDS copy path
-//    (a bounded number of outstanding line requests per CU) is what limits this kernel.
+//    flop of a 256 x 256 tile is two thirds of a 128 x 256 one. Measured by taking parts out:
+//    the copies (their issue, not their latency), the promotion FMAs and the per-block barrier
+//    each cost more than the LDS fragment reads.
 //  * 8 waves (2 per SIMD), each owning 64 x 128 as 4 x 8 fragments of 16 x 16. One
 //    v_mfma_scale_f32_16x16x128_f8f6f4 (scale operands neutral) computes a fragment's whole
-//    128-wide K block, so the partial P is 4 registers and is promoted (4 FMAs) two MFMAs
-//    after it was issued; the 4 A fragments stay in registers for the K block, the 8 B
+//    128-wide K block, so the partial P is 4 registers and is promoted (4 FMAs) three MFMAs
+//    after it was issued, by when it is mostly written (few wait states). Each MFMA, the
+//    promotion that follows it and its LDS reads or copies form one scheduling region, so the
+//    order is the source order. The 4 A fragments stay in registers for the K block, the 8 B
 //    fragments stream through a 3-deep register queue two fragments ahead of their MFMAs.
 //  * operands stream through a 2-stage LDS ring filled by buffer -> LDS copies
 //    (buffer_load_dwordx4 ... lds); 16-byte chunks are XOR-swizzled so fragment reads are free
@@ -220,11 +223,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       float sc[MI];
 #pragma unroll
       for (int i = 0; i < MI; i++) sc[i] = as_raw[i] * bs_raw;
-      v4f part[3];
+      v4f part[4];
       // passes 0..5: B fragment j against the 4 resident A fragments, at raised wave priority so
       // the SIMD's arbiter favours feeding the matrix unit; B fragment j + 2 is read in two
       // halves, after the first and the third MFMA. The promotion of each partial is pinned
-      // right after the MFMA two slots later, which also keeps the MFMAs in their pass. Passes 0
+      // right after the MFMA three slots later, which also keeps the MFMAs in their pass. Passes 0
       // and 1 also copy the A half and B scales of block b+1 into the other stage (freed by the
       // barrier of block b-1; its B half went out in passes 6 and 7 of block b-1).
 #pragma unroll
@@ -235,10 +238,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
         for (int i = 0; i < MI; i++) {
           const int k = j * MI + i;
-          part[k % 3] = mma(bq[j % 3], af[i]);
-          if (k >= 2) {
-            const int kp = k - 2, jp = kp / MI, ip = kp % MI;
-            acc[ip][jp] += part[kp % 3] * sc[ip];
+          part[k % 4] = mma(bq[j % 3], af[i]);
+          if (k >= 3) {
+            const int kp = k - 3, jp = kp / MI, ip = kp % MI;
+            acc[ip][jp] += part[kp % 4] * sc[ip];
             asm volatile("" : "+v"(acc[ip][jp]));
           }
           if (j < 2 && (i & 1)) {
@@ -247,17 +250,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           }
           if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[0]);
           if (j + 2 < NJ && i == 2) hi = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
         if (j + 2 < NJ) bq[(j + 2) % 3] = cat(lo, hi);
-#pragma unroll
-        for (int i = 0; i < MI; i++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          if ((i & 1) == 0 && j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if ((i & 1) == 1 && j < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          if (i == 3 && j == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
       // This wave's reads of stage S are done and its copies of block b+1 have landed; after
@@ -272,21 +268,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 2) * MI + i;
-        part[k % 3] = mma(bq[(NJ - 2) % 3], af[i]);
-        const int kp = k - 2, jp = kp / MI, ip = kp % MI;
-        acc[ip][jp] += part[kp % 3] * sc[ip];
+        part[k % 4] = mma(bq[(NJ - 2) % 3], af[i]);
+        const int kp = k - 3, jp = kp / MI, ip = kp % MI;
+        acc[ip][jp] += part[kp % 4] * sc[ip];
         asm volatile("" : "+v"(acc[ip][jp]));
         if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), i >> 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (b % AS_CHUNK == 0 && b > 0)
         issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
                           wave);
-#pragma unroll
-      for (int i = 0; i < MI; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 2);
-        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);
-      }
       __builtin_amdgcn_sched_barrier(0);
       // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
       // MFMA, then the first two B fragments and the scales of block b+1 are read; copies 2 and 3
@@ -294,14 +285,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 1) * MI + i;
-        part[k % 3] = mma(bq[(NJ - 1) % 3], af[i]);
+        part[k % 4] = mma(bq[(NJ - 1) % 3], af[i]);
         {
-          const int kp = k - 2, jp = kp / MI, ip = kp % MI;
-          acc[ip][jp] += part[kp % 3] * sc[ip];
+          const int kp = k - 3, jp = kp / MI, ip = kp % MI;
+          acc[ip][jp] += part[kp % 4] * sc[ip];
           asm volatile("" : "+v"(acc[ip][jp]));
         }
         af[i] = read_frag(smem + sn_ab + i * 2048, base_a);
         if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), 2 + (i >> 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
       bq[0] = read_frag(smem + sn_ab, base_b);
       bq[1] = read_frag(smem + sn_ab + 2048, base_b);
@@ -313,19 +305,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           as_raw[i] = *(const float*)(smem + (as_v ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
       }
       bs_raw = *(const float*)(smem + sn_bs + base_bs);
-#pragma unroll
-      for (int i = 0; i < MI; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
-        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-      }
       __builtin_amdgcn_sched_barrier(0);
-      // the last two partials of the block
+      // the last three partials of the block
 #pragma unroll
-      for (int k = MI * NJ - 2; k < MI * NJ; k++) {
+      for (int k = MI * NJ - 3; k < MI * NJ; k++) {
         const int jp = k / MI, ip = k % MI;
-        acc[ip][jp] += part[k % 3] * sc[ip];
+        acc[ip][jp] += part[k % 4] * sc[ip];
         asm volatile("" : "+v"(acc[ip][jp]));
       }
     }
