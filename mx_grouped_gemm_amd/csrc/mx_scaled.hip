@@ -100,17 +100,18 @@ struct MxLoadPlan {
   int a_dst, b_dst;
 };
 
+// Copy i (of A_INSTR / B_INSTR per wave) of K block kb into the A or B half of a stage.
 template <int FA, int FB>
-__device__ __forceinline__ void mx_issue(uint8_t* __restrict__ da, uint8_t* __restrict__ db,
-                                         const MxLoadPlan<FA, FB>& lp, int kb) {
+__device__ __forceinline__ void mx_copy_a(uint8_t* __restrict__ da, const MxLoadPlan<FA, FB>& lp, int kb, int i) {
   using L = Layout<FA, FB>;
-  kb = __builtin_amdgcn_readfirstlane(kb);
-#pragma unroll
-  for (int i = 0; i < L::A_INSTR; i++)
-    buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)kb * L::RA, as_lds(da + lp.a_dst + i * 1024));
-#pragma unroll
-  for (int i = 0; i < L::B_INSTR; i++)
-    buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)kb * L::RB, as_lds(db + lp.b_dst + i * 1024));
+  buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RA,
+            as_lds(da + lp.a_dst + i * 1024));
+}
+template <int FA, int FB>
+__device__ __forceinline__ void mx_copy_b(uint8_t* __restrict__ db, const MxLoadPlan<FA, FB>& lp, int kb, int i) {
+  using L = Layout<FA, FB>;
+  buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RB,
+            as_lds(db + lp.b_dst + i * 1024));
 }
 
 // Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows into
@@ -210,11 +211,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 #pragma unroll
       for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: scale chunks 0 and 1, blocks 0 and 1 in flight; block 0 published
+    // prologue: scale chunks 0 and 1, block 0 and the B half of block 1 (its A half goes out in
+    // passes 0 and 1 of block 0, as in every block); block 0 published
     mx_issue_scales<FA, FB>(smem + L::SA_REGION, smem + L::SB_REGION, lp, 0, wave);
     mx_issue_scales<FA, FB>(smem + L::SA_REGION + SC_BYTES, smem + L::SB_REGION + SC_BYTES, lp, 1, wave);
-    mx_issue<FA, FB>(smem + L::A_REGION, smem + L::B_REGION, lp, 0);
-    mx_issue<FA, FB>(smem + L::A_REGION + L::A_BYTES, smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1));
+#pragma unroll
+    for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB>(smem + L::A_REGION, lp, 0, i);
+#pragma unroll
+    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB>(smem + L::B_REGION, lp, 0, i);
+#pragma unroll
+    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB>(smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1), i);
     wait_vmcnt<0>();
     barrier();
 
@@ -242,23 +248,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
     sbq[0] = scale_b(0, 0);
     sbq[1] = scale_b(0, 1);
 
+    // copies per wave and pass: the A half of a block over passes 0 and 1, the B half over
+    // passes 6 and 7, each after the second or fourth MFMA of the pass
+    constexpr int A_PP = L::A_INSTR / 2, B_PP = L::B_INSTR / 2;
+    static_assert(A_PP >= 1 && A_PP <= 2 && B_PP >= 1 && B_PP <= 2, "copy schedule");
+
     for (int b = 0; b < KB; b++) {
       const int S = b & 1;
       const int soa = S * L::A_BYTES, sob = S * L::B_BYTES;                 // this block's stage
       const int sna = (S ^ 1) * L::A_BYTES, snb = (S ^ 1) * L::B_BYTES;
       const int bn = min(b + 1, KB - 1);
-      // passes 0..6: B fragment j against the 4 resident A fragments; B fragment j + 2 and its
-      // scale are read at the start of pass j
+      // passes 0..5: B fragment j against the 4 resident A fragments, MFMAs at raised wave
+      // priority; B fragment j + 2 is read in two halves (after the first and third MFMA) and
+      // its scale after the third. Passes 0 and 1 also copy the A half of block b+1 into the
+      // other stage (freed by the barrier of block b-1; its B half went out in passes 6 and 7
+      // of block b-1). Each MFMA with what follows it is a scheduling region of its own.
 #pragma unroll
-      for (int j = 0; j < NJ - 1; j++) {
+      for (int j = 0; j < NJ - 2; j++) {
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 2 < NJ) {
-          bq[(j + 2) % 3] = read_frag<L::RB>(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB, fb);
-          sbq[(j + 2) % 3] = scale_b(b, j + 2);
-        }
+        v4i lo, hi;
+        int sbn = 0;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int i = 0; i < MI; i++)
+        for (int i = 0; i < MI; i++) {
           acc[i][j] = mma<FA, FB>(bq[j % 3], af[i], acc[i][j], sbq[j % 3], sa[i]);
+          if (j < 2 && (i & 1) && (i >> 1) < A_PP)
+            mx_copy_a<FA, FB>(smem + L::A_REGION + sna, lp, bn, j * A_PP + (i >> 1));
+          if (j + 2 < NJ && i == 0) lo = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[0]);
+          if (j + 2 < NJ && i == 2) {
+            if constexpr (L::RB == 128) hi = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[1]);
+            sbn = scale_b(b, j + 2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        if (j + 2 < NJ) {
+          if constexpr (L::RB == 128) bq[(j + 2) % 3] = cat(lo, hi);
+          else bq[(j + 2) % 3] = (v8i){lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+          sbq[(j + 2) % 3] = sbn;
+        }
         // pin the previous pass's MFMAs (complete by now) ahead of this point, so that the
         // compiler does not sink them past the loop's branch
         if (j > 0) {
@@ -267,7 +295,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // stage S fully read, block b+1 landed: publish it, then refill stage S
+      // stage S fully read (its last read was in pass 5), block b+1 landed: publish it
       wait_vmcnt<0>();
       wait_lds_reads();
       barrier();
@@ -277,25 +305,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         mx_issue_scales<FA, FB>(smem + L::SA_REGION + cb, smem + L::SB_REGION + cb, lp, b / SC_CHUNK + 1, wave);
       }
 #pragma unroll
-      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
+      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 3]));
       __builtin_amdgcn_sched_barrier(0);
+      // pass 6 with the first copies of the B half of block b+2 into stage S (past the last
+      // block they repeat block KB-1 into a stage that is not read again)
+#pragma unroll
+      for (int i = 0; i < MI; i++) {
+        acc[i][NJ - 2] = mma<FA, FB>(bq[(NJ - 2) % 3], af[i], acc[i][NJ - 2], sbq[(NJ - 2) % 3], sa[i]);
+        if ((i & 1) && (i >> 1) < B_PP)
+          mx_copy_b<FA, FB>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), i >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // pass 7: last B fragment; each A fragment and its scale are refilled from block b+1
-      // right after their MFMA; the first two B fragments of block b+1 and their scales are
-      // read; copies of block b+2 into stage S (past the last block they repeat block KB-1
-      // into a stage not read again)
+      // right after their MFMA; the rest of the B half of block b+2; then the first two B
+      // fragments of block b+1 and their scales are read
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         acc[i][NJ - 1] = mma<FA, FB>(bq[(NJ - 1) % 3], af[i], acc[i][NJ - 1], sbq[(NJ - 1) % 3], sa[i]);
         af[i] = read_frag<L::RA>(smem + L::A_REGION + sna + i * 16 * L::RA, fa);
         sa[i] = scale_a(bn, i);
+        if ((i & 1) && (i >> 1) < B_PP)
+          mx_copy_b<FA, FB>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), B_PP + (i >> 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
       bq[0] = read_frag<L::RB>(smem + L::B_REGION + snb, fb);
       bq[1] = read_frag<L::RB>(smem + L::B_REGION + snb + 16 * L::RB, fb);
       sbq[0] = scale_b(bn, 0);
       sbq[1] = scale_b(bn, 1);
-      mx_issue<FA, FB>(smem + L::A_REGION + soa, smem + L::B_REGION + sob, lp, min(b + 2, KB - 1));
 #pragma unroll
-      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 1]));
+      for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();
