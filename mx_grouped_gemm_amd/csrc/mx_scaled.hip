@@ -38,9 +38,11 @@ template <int F> struct Elem;
 template <> struct Elem<1> { static constexpr int kRowBytes = 128; static constexpr int kCode = 0; };
 template <> struct Elem<2> { static constexpr int kRowBytes = 64; static constexpr int kCode = 4; };
 
-template <int FA, int FB>
+// KS: 128-K sub-blocks per stage of the LDS ring (2 for e2m1 x e2m1, so that a stage holds as
+// many bytes and MFMA work as an e4m3 one). RA / RB: bytes of one tile row in a stage.
+template <int FA, int FB, int KS>
 struct Layout {
-  static constexpr int RA = Elem<FA>::kRowBytes, RB = Elem<FB>::kRowBytes;
+  static constexpr int RA = Elem<FA>::kRowBytes * KS, RB = Elem<FB>::kRowBytes * KS;
   static constexpr int A_BYTES = BM * RA, B_BYTES = BN * RB;       // per stage
   static constexpr int A_REGION = 0;
   static constexpr int B_REGION = STAGES * A_BYTES;
@@ -91,34 +93,34 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* p, const FragBase<ROWB>&
   }
 }
 
-template <int FA, int FB>
+template <int FA, int FB, int KS>
 struct MxLoadPlan {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
-  uint32_t a_voff[Layout<FA, FB>::A_INSTR], b_voff[Layout<FA, FB>::B_INSTR];
+  uint32_t a_voff[Layout<FA, FB, KS>::A_INSTR], b_voff[Layout<FA, FB, KS>::B_INSTR];
   uint32_t sc_voff_a, sc_voff_b;   // scale chunk: lane part (row and dword inside the chunk)
   uint32_t sc_row8_a, sc_row8_b;   // scale chunk: bytes of 8 rows of the scale tensors
   int a_dst, b_dst;
 };
 
 // Copy i (of A_INSTR / B_INSTR per wave) of K block kb into the A or B half of a stage.
-template <int FA, int FB>
-__device__ __forceinline__ void mx_copy_a(uint8_t* __restrict__ da, const MxLoadPlan<FA, FB>& lp, int kb, int i) {
-  using L = Layout<FA, FB>;
+template <int FA, int FB, int KS>
+__device__ __forceinline__ void mx_copy_a(uint8_t* __restrict__ da, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
+  using L = Layout<FA, FB, KS>;
   buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RA,
             as_lds(da + lp.a_dst + i * 1024));
 }
-template <int FA, int FB>
-__device__ __forceinline__ void mx_copy_b(uint8_t* __restrict__ db, const MxLoadPlan<FA, FB>& lp, int kb, int i) {
-  using L = Layout<FA, FB>;
+template <int FA, int FB, int KS>
+__device__ __forceinline__ void mx_copy_b(uint8_t* __restrict__ db, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
+  using L = Layout<FA, FB, KS>;
   buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RB,
             as_lds(db + lp.b_dst + i * 1024));
 }
 
 // Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows into
 // [row][8 dwords] layouts; wave w copies rows 32 w .. 32 w + 31 of each.
-template <int FA, int FB>
+template <int FA, int FB, int KS>
 __device__ __forceinline__ void mx_issue_scales(uint8_t* __restrict__ dsa, uint8_t* __restrict__ dsb,
-                                                const MxLoadPlan<FA, FB>& lp, int chunk, int wave) {
+                                                const MxLoadPlan<FA, FB, KS>& lp, int chunk, int wave) {
   const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * SC_CHUNK * 4;
 #pragma unroll
   for (int i = 0; i < SC_INSTR; i++) {
@@ -133,9 +135,18 @@ __device__ __forceinline__ v4f mma(const v8i& b, const v8i& a, const v4f& c, int
                                                           0, sb, 0, sa);
 }
 
-template <int FA, int FB, int OUT>
+// Operand of sub-block h of a fragment read as two 16-byte chunks: with two e2m1 sub-blocks per
+// stage, chunk q holds sub-block 0 and chunk 4 + q sub-block 1 of the lane's 32-K slice (the
+// instruction reads 4 registers of an e2m1 operand, so the unused half costs nothing).
+template <int KS>
+__device__ __forceinline__ v8i sub_op(const v8i& x, int h) {
+  if constexpr (KS == 1) return x;
+  else return h == 0 ? x : (v8i){x[4], x[5], x[6], x[7], 0, 0, 0, 0};
+}
+
+template <int FA, int FB, int OUT, int KS>
 __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_blocks) {
-  using L = Layout<FA, FB>;
+  using L = Layout<FA, FB, KS>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -143,8 +154,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
   const int num_super = (p.num_tiles + 1) / 2;
   int s, nb;
   if (!work_item(num_super, n_blocks, 8, s, nb)) return;
-  const int n0 = nb * BN, N = p.N, KB = p.K / BK;
-  const size_t rowA = (size_t)p.K * L::RA / BK, rowB = (size_t)p.K * L::RB / BK;   // bytes per row
+  const int n0 = nb * BN, N = p.N, KB = p.K / (BK * KS);          // stages
+  const size_t rowA = (size_t)p.K * Elem<FA>::kRowBytes / BK;      // bytes per row
+  const size_t rowB = (size_t)p.K * Elem<FB>::kRowBytes / BK;
+  constexpr int SCS = SC_CHUNK / KS;                                // stages per scale chunk
   const size_t srow = (size_t)p.K / 32;                                            // scale bytes per row
   const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
   const int r16 = lane & 15, q = lane >> 4;
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 
     // Copy plan. Every row offset is in the per-lane offset, which the resource bounds check:
     // rows past the pass or past N read as zero.
-    MxLoadPlan<FA, FB> lp;
+    MxLoadPlan<FA, FB, KS> lp;
     lp.a_rsrc = make_rsrc((const uint8_t*)p.A + (size_t)row0 * rowA, (uint64_t)rows * rowA);
     lp.b_rsrc = make_rsrc((const uint8_t*)p.B + ((size_t)e * N + n0) * rowB, (uint64_t)ncols * rowB);
     lp.sa_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)row0 * srow, (uint64_t)rows * srow);
@@ -213,40 +226,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 
     // prologue: scale chunks 0 and 1, block 0 and the B half of block 1 (its A half goes out in
     // passes 0 and 1 of block 0, as in every block); block 0 published
-    mx_issue_scales<FA, FB>(smem + L::SA_REGION, smem + L::SB_REGION, lp, 0, wave);
-    mx_issue_scales<FA, FB>(smem + L::SA_REGION + SC_BYTES, smem + L::SB_REGION + SC_BYTES, lp, 1, wave);
+    mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION, smem + L::SB_REGION, lp, 0, wave);
+    mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION + SC_BYTES, smem + L::SB_REGION + SC_BYTES, lp, 1, wave);
 #pragma unroll
-    for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB>(smem + L::A_REGION, lp, 0, i);
+    for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB, KS>(smem + L::A_REGION, lp, 0, i);
 #pragma unroll
-    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB>(smem + L::B_REGION, lp, 0, i);
+    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB, KS>(smem + L::B_REGION, lp, 0, i);
 #pragma unroll
-    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB>(smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1), i);
+    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB, KS>(smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1), i);
     wait_vmcnt<0>();
     barrier();
 
     // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, moved to byte 0
-    auto scale_a = [&](int kb, int i) {
-      const int so = ((kb / SC_CHUNK) & 1) * SC_BYTES + (kb % SC_CHUNK) * 4;
+    // g: 128-K sub-block index (stage b holds sub-blocks KS b .. KS b + KS - 1)
+    auto scale_a = [&](int g, int i) {
+      const int so = ((g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
       return (int)(*(const uint32_t*)(smem + base_sa + so + i * 16 * SC_CHUNK * 4) >> (8 * q));
     };
-    auto scale_b = [&](int kb, int j) {
-      const int so = ((kb / SC_CHUNK) & 1) * SC_BYTES + (kb % SC_CHUNK) * 4;
+    auto scale_b = [&](int g, int j) {
+      const int so = ((g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
       return (int)(*(const uint32_t*)(smem + base_sb + so + j * 16 * SC_CHUNK * 4) >> (8 * q));
     };
 
     // A fragments and scales of the block stay in registers; B fragments and their scales
     // stream through 3-deep queues two fragments ahead
     v8i af[MI], bq[3];
-    int sa[MI], sbq[3];
+    int sa[MI][KS], sbq[3][KS];
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       af[i] = read_frag<L::RA>(smem + L::A_REGION + i * 16 * L::RA, fa);
-      sa[i] = scale_a(0, i);
+#pragma unroll
+      for (int h = 0; h < KS; h++) sa[i][h] = scale_a(h, i);
     }
     bq[0] = read_frag<L::RB>(smem + L::B_REGION, fb);
     bq[1] = read_frag<L::RB>(smem + L::B_REGION + 16 * L::RB, fb);
-    sbq[0] = scale_b(0, 0);
-    sbq[1] = scale_b(0, 1);
+#pragma unroll
+    for (int h = 0; h < KS; h++) {
+      sbq[0][h] = scale_b(h, 0);
+      sbq[1][h] = scale_b(h, 1);
+    }
 
     // copies per wave and pass: the A half of a block over passes 0 and 1, the B half over
     // passes 6 and 7, each after the second or fourth MFMA of the pass
@@ -258,8 +276,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       const int soa = S * L::A_BYTES, sob = S * L::B_BYTES;                 // this block's stage
       const int sna = (S ^ 1) * L::A_BYTES, snb = (S ^ 1) * L::B_BYTES;
       const int bn = min(b + 1, KB - 1);
-      // passes 0..5: B fragment j against the 4 resident A fragments, MFMAs at raised wave
-      // priority; B fragment j + 2 is read in two halves (after the first and third MFMA) and
+      // passes 0..5: B fragment j against the 4 resident A fragments (with two sub-blocks per
+      // stage: sub-block 0 for all four, then sub-block 1, so chained MFMAs are four apart), MFMAs
+      // at raised wave priority; B fragment j + 2 is read in two halves (after the first and third MFMA) and
       // its scale after the third. Passes 0 and 1 also copy the A half of block b+1 into the
       // other stage (freed by the barrier of block b-1; its B half went out in passes 6 and 7
       // of block b-1). Each MFMA with what follows it is a scheduling region of its own.
@@ -267,17 +286,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       for (int j = 0; j < NJ - 2; j++) {
         __builtin_amdgcn_sched_barrier(0);
         v4i lo, hi;
-        int sbn = 0;
+        int sbn[KS];
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
+        for (int h = 0; h < KS; h++)
+#pragma unroll
         for (int i = 0; i < MI; i++) {
-          acc[i][j] = mma<FA, FB>(bq[j % 3], af[i], acc[i][j], sbq[j % 3], sa[i]);
+          acc[i][j] = mma<FA, FB>(sub_op<KS>(bq[j % 3], h), sub_op<KS>(af[i], h), acc[i][j], sbq[j % 3][h], sa[i][h]);
+          if (h < KS - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            continue;
+          }
           if (j < 2 && (i & 1) && (i >> 1) < A_PP)
-            mx_copy_a<FA, FB>(smem + L::A_REGION + sna, lp, bn, j * A_PP + (i >> 1));
+            mx_copy_a<FA, FB, KS>(smem + L::A_REGION + sna, lp, bn, j * A_PP + (i >> 1));
           if (j + 2 < NJ && i == 0) lo = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[0]);
           if (j + 2 < NJ && i == 2) {
             if constexpr (L::RB == 128) hi = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[1]);
-            sbn = scale_b(b, j + 2);
+#pragma unroll
+            for (int h = 0; h < KS; h++) sbn[h] = scale_b(KS * b + h, j + 2);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -285,7 +311,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         if (j + 2 < NJ) {
           if constexpr (L::RB == 128) bq[(j + 2) % 3] = cat(lo, hi);
           else bq[(j + 2) % 3] = (v8i){lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-          sbq[(j + 2) % 3] = sbn;
+#pragma unroll
+          for (int h = 0; h < KS; h++) sbq[(j + 2) % 3][h] = sbn[h];
         }
         // pin the previous pass's MFMAs (complete by now) ahead of this point, so that the
         // compiler does not sink them past the loop's branch
@@ -300,9 +327,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       wait_lds_reads();
       barrier();
       // scales of chunk c+1 replace those of chunk c-1 while block 8c is computed
-      if (b % SC_CHUNK == 0 && b > 0) {
-        const int cb = ((b / SC_CHUNK + 1) & 1) * SC_BYTES;
-        mx_issue_scales<FA, FB>(smem + L::SA_REGION + cb, smem + L::SB_REGION + cb, lp, b / SC_CHUNK + 1, wave);
+      if (b % SCS == 0 && b > 0) {
+        const int cb = ((b / SCS + 1) & 1) * SC_BYTES;
+        mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION + cb, smem + L::SB_REGION + cb, lp, b / SCS + 1, wave);
       }
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 3]));
@@ -310,28 +337,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       // pass 6 with the first copies of the B half of block b+2 into stage S (past the last
       // block they repeat block KB-1 into a stage that is not read again)
 #pragma unroll
+      for (int h = 0; h < KS; h++)
+#pragma unroll
       for (int i = 0; i < MI; i++) {
-        acc[i][NJ - 2] = mma<FA, FB>(bq[(NJ - 2) % 3], af[i], acc[i][NJ - 2], sbq[(NJ - 2) % 3], sa[i]);
-        if ((i & 1) && (i >> 1) < B_PP)
-          mx_copy_b<FA, FB>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), i >> 1);
+        acc[i][NJ - 2] = mma<FA, FB>(sub_op<KS>(bq[(NJ - 2) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 2],
+                                     sbq[(NJ - 2) % 3][h], sa[i][h]);
+        if ((i & 1) && (i >> 1) < B_PP && h == KS - 1)
+          mx_copy_b<FA, FB, KS>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), i >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       // pass 7: last B fragment; each A fragment and its scale are refilled from block b+1
       // right after their MFMA; the rest of the B half of block b+2; then the first two B
       // fragments of block b+1 and their scales are read
 #pragma unroll
+      for (int h = 0; h < KS; h++)
+#pragma unroll
       for (int i = 0; i < MI; i++) {
-        acc[i][NJ - 1] = mma<FA, FB>(bq[(NJ - 1) % 3], af[i], acc[i][NJ - 1], sbq[(NJ - 1) % 3], sa[i]);
+        acc[i][NJ - 1] = mma<FA, FB>(sub_op<KS>(bq[(NJ - 1) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 1],
+                                     sbq[(NJ - 1) % 3][h], sa[i][h]);
+        if (h < KS - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         af[i] = read_frag<L::RA>(smem + L::A_REGION + sna + i * 16 * L::RA, fa);
-        sa[i] = scale_a(bn, i);
+#pragma unroll
+        for (int h = 0; h < KS; h++) sa[i][h] = scale_a(KS * bn + h, i);
         if ((i & 1) && (i >> 1) < B_PP)
-          mx_copy_b<FA, FB>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), B_PP + (i >> 1));
+          mx_copy_b<FA, FB, KS>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), B_PP + (i >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       bq[0] = read_frag<L::RB>(smem + L::B_REGION + snb, fb);
       bq[1] = read_frag<L::RB>(smem + L::B_REGION + snb + 16 * L::RB, fb);
-      sbq[0] = scale_b(bn, 0);
-      sbq[1] = scale_b(bn, 1);
+#pragma unroll
+      for (int h = 0; h < KS; h++) {
+        sbq[0][h] = scale_b(KS * bn + h, 0);
+        sbq[1][h] = scale_b(KS * bn + h, 1);
+      }
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
       __builtin_amdgcn_sched_barrier(0);
@@ -354,13 +395,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
   }
 }
 
-template <int FA, int FB>
+template <int FA, int FB, int KS = 1>
 hipError_t launch_fmt(const GemmArgs& a, int out, hipStream_t stream, dim3 grid, int n_blocks) {
   dim3 block(NTHREADS);
   switch (out) {
-    case kOutF32: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF32>), grid, block, 0, stream, a, n_blocks); break;
-    case kOutBF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutBF16>), grid, block, 0, stream, a, n_blocks); break;
-    case kOutF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF16>), grid, block, 0, stream, a, n_blocks); break;
+    case kOutF32: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF32, KS>), grid, block, 0, stream, a, n_blocks); break;
+    case kOutBF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutBF16, KS>), grid, block, 0, stream, a, n_blocks); break;
+    case kOutF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF16, KS>), grid, block, 0, stream, a, n_blocks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -377,7 +418,11 @@ hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream
   if (fmt_a == 1 && fmt_b == 1) return launch_fmt<1, 1>(a, out, stream, grid, n_blocks);
   if (fmt_a == 1 && fmt_b == 2) return launch_fmt<1, 2>(a, out, stream, grid, n_blocks);
   if (fmt_a == 2 && fmt_b == 1) return launch_fmt<2, 1>(a, out, stream, grid, n_blocks);
-  if (fmt_a == 2 && fmt_b == 2) return launch_fmt<2, 2>(a, out, stream, grid, n_blocks);
+  if (fmt_a == 2 && fmt_b == 2) {
+    // 256-K stages when K is a multiple of 256
+    if ((a.K / BK) % 2 == 0) return launch_fmt<2, 2, 2>(a, out, stream, grid, n_blocks);
+    return launch_fmt<2, 2, 1>(a, out, stream, grid, n_blocks);
+  }
   return hipErrorInvalidValue;
 }
 

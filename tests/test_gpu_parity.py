@@ -222,6 +222,15 @@ def test_mx_small(fa, fb, out):
     check(p, out, C, label=f"mx {fa}x{fb}")
 
 
+@pytest.mark.parametrize("K", [256, 384, 1280, 2304])
+def test_mx_e2m1_k_depths(K):
+    """e2m1 x e2m1 stages hold two 128-K blocks when K is a multiple of 256 (one stage, 5 stages
+    with a scale chunk ending mid-way, 9 stages); K = 384 takes one-block stages."""
+    p = mx_problem(256, 256, K, "e2m1", "e2m1", device="cuda", seed=K)
+    C, _, _ = run_problem(p, "f32")
+    check(p, "f32", C, label=f"mx e2m1xe2m1 K={K}")
+
+
 @pytest.mark.parametrize("fa,fb", MX_PAIRS)
 def test_mx_exact_products_bit_exact(fa, fb):
     """Layout pin for elements, nibble order and per-32 scales: small values and scales near 1
