@@ -16,6 +16,11 @@ With --workload mx8192_<a>_<b> a step is instead one dense MX GEMM of 8192^3 (e8
 32 K, fp16 out) with formats a x b; its roofline is that launch against the peak of the
 narrower-rate format pair.
 
+With --workload permute_moe32 a step is the step before the GEMM on the same routing: per-expert
+counts of the top-8 picks, the tile map, and the permutation of the 16384 bf16 token rows
+(K = 7168) into the padded expert-sorted A with e4m3 1x128 quantisation. It is HBM-bound: the
+value is GB/s of algorithmic bytes and the roofline is against the 8 TB/s HBM peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload W]
        python bench.py --copy-calibration MIB --steps K   (HBM counter calibration)
 """
@@ -58,7 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="moe32",
-                    choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1"])
+                    choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
+                             "permute_moe32"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB "
                          "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
@@ -167,6 +173,104 @@ def bench_mx(args, torch, bsg, make_problem):
     print(json.dumps(out), flush=True)
 
 
+def permute_bytes(tokens, top_k, K, M):
+    """Algorithmic bytes of one quantise-and-permute call: bf16 token rows read once, every row
+    of the grouped A (codes and scales, padding included) written once, picks read and their
+    rows written once."""
+    return tokens * K * 2 + M * K + M * (K // 128) * 4 + 2 * tokens * top_k * 4
+
+
+def cpu_baseline_permute(x, ids, eo, M, sample=1024):
+    """Time the oracle's quantise-and-permute on the first ``sample`` tokens."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import permute as op
+
+    xs = x[:sample].float().cpu().numpy()
+    ids_s = ids[:sample]
+    counts = op.route_counts(ids_s, len(eo) - 1)
+    offs = np.concatenate([[0], np.cumsum(-(-counts // 128) * 128)])
+    Ms = int(offs[-1])
+    t0 = time.perf_counter()
+    op.quantize_permute(xs, ids_s, offs, Ms)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    nbytes = permute_bytes(sample, ids.shape[1], xs.shape[1], Ms)
+    return {
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"first {sample} of {x.shape[0]} tokens (their {sample * ids.shape[1]} picks), "
+                  f"oracle quantise + permute; {dt:.1f} s",
+    }
+
+
+def bench_permute(args, torch, bsg):
+    """A step: route counts, tile map, and quantise + permute of the 32-expert MoE activations."""
+    from workloads.generate import MOE32, activations, routing_counts, routing_topk
+
+    T, k, E, K = MOE32["tokens"], MOE32["top_k"], MOE32["experts"], 7168
+    counts_h = routing_counts(seed=args.seed, **MOE32)
+    ids_h = routing_topk(counts_h, T, k, seed=args.seed)
+    T_tiles = int(sum(-(-int(c) // 128) for c in counts_h))
+    M = 128 * T_tiles
+    x = activations(T, K, device="cuda", seed=args.seed)
+    ids = torch.from_numpy(ids_h).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    eo = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    to = torch.empty(T_tiles + 1, dtype=torch.int32, device="cuda")
+    ei = torch.empty(T_tiles, dtype=torch.int32, device="cuda")
+    dest = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    launches = []
+
+    def step(record):
+        bsg.bsgemm_route_counts(ids, E, counts=counts, stream=stream)
+        bsg.bsgemm_build_tiles(counts, T_tiles, padded=True, expert_offsets=eo, tile_offsets=to,
+                               expert_ids=ei, stream=stream)
+        a = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            a.record(stream)
+        bsg.bsgemm_quantize_permute(x, ids, eo, M, E, dest=dest, qa=qa, a_scales=sa, stream=stream)
+        if record:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            launches.append((a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in launches]))
+    nbytes = permute_bytes(T, k, K, M)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "GB/s, quantise (e4m3, 1x128 fp32 scales) + permute of MoE token activations "
+                  "into the grouped GEMM's A",
+        "value": round(value, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
+        "config": {"workload": f"permute_moe32: {T} tokens x top-{k} over {E} experts (Dirichlet(1.0), "
+                               f"2 empty), bf16 rows of K={K} -> {M} padded rows of e4m3",
+                   "tokens": T, "top_k": k, "experts": E, "K": K, "padded_rows": M, "seed": args.seed},
+        "kernels_ms": {"quantize_permute": round(call_ms, 4)},
+        "roofline": {
+            "kernel": "permute_rank_kernel + quantize_kernel (one bsgemm_quantize_permute call)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_permute(x, ids_h, eo.cpu().numpy(), M)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -196,6 +300,9 @@ def main():
     torch.cuda.set_device(dev)
     bsg.load_library()
 
+    if args.workload == "permute_moe32":
+        bench_permute(args, torch, bsg)
+        return
     if args.workload != "moe32":
         bench_mx(args, torch, bsg, make_problem)
         return

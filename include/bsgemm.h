@@ -120,6 +120,58 @@ int bsgemm_grouped(const void* A, const void* a_scales, const void* B, const voi
                    void* C, int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
                    void* stream);
 
+/*
+ * bsgemm_route_counts - picks per expert: the row counts of the grouped A.
+ *
+ * Passage: "promote_accumulators", section Args, argument expert_ids (each group of A's rows
+ * belongs to one expert) - the counts that bsgemm_build_tiles turns into the group layout.
+ *
+ *   topk_ids    DEVICE int32[num_picks]: expert of each pick, usually [tokens, top_k]
+ *               row-major. Ids outside [0, num_experts) are not counted.
+ *   num_picks   >= 0
+ *   num_experts 1 .. 4096
+ *   counts      DEVICE int32[num_experts] (output; overwritten)
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN (int32 alignment), BSG_ERR_DEVICE,
+ * BSG_ERR_LAUNCH.
+ */
+int bsgemm_route_counts(const int32_t* topk_ids, int32_t num_picks, int32_t num_experts,
+                        int32_t* counts, void* stream);
+
+/*
+ * bsgemm_quantize_permute - token activations and top-k picks -> the grouped GEMM's A operand.
+ *
+ * Passage: "promote_accumulators", section Args (A's rows grouped by expert through
+ * expert_ids; an fp32 scale per row per 128 K-elements, the 1x128 block scaling of the FP8
+ * operands). The pages do not order rows inside a group; here expert e's picks fill rows
+ * expert_offsets[e], expert_offsets[e] + 1, ... in pick order (token-major), which makes the
+ * layout unique.
+ *
+ *   dest[t, j]   = A row of pick (t, j), or -1 if its id is outside [0, num_experts) or the
+ *                  row would be >= M
+ *   per token t and 128-block b of x[t]:  s = amax / 448 (1 if amax = 0),
+ *                  q = round-to-nearest-even e4m3fn of clamp(x / s, -448, 448), both divisions
+ *                  in fp32; qa[dest[t, j], block b] = q and a_scales[dest[t, j], b] = s
+ *   rows expert_offsets[e] + count_e .. expert_offsets[e + 1] - 1 (below M): zero codes,
+ *                  scale 1 (the group's padding); all other rows of qa / a_scales untouched
+ *
+ *   x              DEVICE [tokens, K] fp32 or bf16 (x_dtype BSG_OUT_F32 / BSG_OUT_BF16),
+ *                  finite values. 16-byte aligned.
+ *   topk_ids       DEVICE int32[tokens, top_k]
+ *   tokens >= 0, top_k >= 1, K > 0 a multiple of 128, num_experts 1 .. 4096
+ *   expert_offsets DEVICE int32[num_experts + 1], as written by bsgemm_build_tiles from
+ *                  bsgemm_route_counts' counts (padded: each group a multiple of 128 rows)
+ *   M              rows of qa / a_scales (>= 0)
+ *   dest           DEVICE int32[tokens, top_k] (output)
+ *   qa             DEVICE uint8[M, K] e4m3fn codes (output), 16-byte aligned
+ *   a_scales       DEVICE float[M, K/128] (output)
+ * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN, BSG_ERR_FMT (x_dtype), BSG_ERR_DEVICE,
+ * BSG_ERR_LAUNCH.
+ */
+int bsgemm_quantize_permute(const void* x, uint32_t x_dtype, const int32_t* topk_ids,
+                            int32_t tokens, int32_t top_k, int32_t K, int32_t num_experts,
+                            const int32_t* expert_offsets, int32_t M, int32_t* dest, void* qa,
+                            float* a_scales, void* stream);
+
 /* Static, human-readable text for a bsg_status value (never NULL). */
 const char* bsgemm_status_string(int status);
 

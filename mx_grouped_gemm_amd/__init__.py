@@ -13,7 +13,8 @@ import torch
 
 __all__ = [
     "BsgemmError", "ELEM", "SCALE", "OUT", "make_fmt", "bsgemm_build_tiles", "bsgemm_grouped",
-    "bsgemm_status_string", "library_path", "load_library",
+    "bsgemm_status_string", "bsgemm_route_counts", "bsgemm_quantize_permute", "library_path",
+    "load_library",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -24,7 +25,8 @@ ELEM = {"e4m3": 1, "e2m1": 2}
 SCALE = {"blockwise": 1, "mx": 2}
 OUT = {"f32": 1, "bf16": 2, "f16": 3}
 OUT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-EXPORTED = ("bsgemm_build_tiles", "bsgemm_grouped", "bsgemm_status_string")
+EXPORTED = ("bsgemm_build_tiles", "bsgemm_grouped", "bsgemm_status_string", "bsgemm_route_counts",
+            "bsgemm_quantize_permute")
 
 
 class BsgemmError(RuntimeError):
@@ -52,6 +54,10 @@ def load_library():
     lib.bsgemm_grouped.restype = ctypes.c_int
     lib.bsgemm_status_string.argtypes = [ctypes.c_int]
     lib.bsgemm_status_string.restype = ctypes.c_char_p
+    lib.bsgemm_route_counts.argtypes = [vp, i32, i32, vp, vp]
+    lib.bsgemm_route_counts.restype = ctypes.c_int
+    lib.bsgemm_quantize_permute.argtypes = [vp, u32, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
+    lib.bsgemm_quantize_permute.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -130,3 +136,46 @@ def bsgemm_grouped(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, 
     if st != 0:
         raise BsgemmError("bsgemm_grouped", st)
     return C
+
+
+def bsgemm_route_counts(topk_ids, num_experts, counts=None, stream=None):
+    """Picks per expert from int32 top-k ids (device tensor, any shape). Returns ``counts``."""
+    _dev(topk_ids, "topk_ids", torch.int32)
+    if counts is None:
+        counts = torch.empty(num_experts, dtype=torch.int32, device=topk_ids.device)
+    _dev(counts, "counts", torch.int32)
+    st = load_library().bsgemm_route_counts(_ptr(topk_ids), topk_ids.numel(), int(num_experts),
+                                            _ptr(counts), _stream(stream))
+    if st != 0:
+        raise BsgemmError("bsgemm_route_counts", st)
+    return counts
+
+
+def bsgemm_quantize_permute(x, topk_ids, expert_offsets, M, num_experts, dest=None, qa=None,
+                            a_scales=None, stream=None):
+    """Quantise token rows ``x`` ([tokens, K], fp32 or bf16) to e4m3 with 1x128 scales and place
+    them at the rows of their top-k picks (``topk_ids`` int32 [tokens, top_k]) in the grouped
+    layout given by ``expert_offsets``. Returns (dest, qa, a_scales)."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    _dev(x, "x")
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(expert_offsets, "expert_offsets", torch.int32)
+    tokens, K = x.shape
+    top_k = topk_ids.shape[1]
+    dev = x.device
+    if dest is None:
+        dest = torch.empty(tokens, top_k, dtype=torch.int32, device=dev)
+    if qa is None:
+        qa = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    if a_scales is None:
+        a_scales = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    for t, n in ((dest, "dest"), (qa, "qa"), (a_scales, "a_scales")):
+        _dev(t, n)
+    x_dtype = OUT["f32"] if x.dtype == torch.float32 else OUT["bf16"]
+    st = load_library().bsgemm_quantize_permute(
+        _ptr(x), x_dtype, _ptr(topk_ids), int(tokens), int(top_k), int(K), int(num_experts),
+        _ptr(expert_offsets), int(M), _ptr(dest), _ptr(qa), _ptr(a_scales), _stream(stream))
+    if st != 0:
+        raise BsgemmError("bsgemm_quantize_permute", st)
+    return dest, qa, a_scales

@@ -69,6 +69,39 @@ extern "C" int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, in
   return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
 }
 
+extern "C" int bsgemm_route_counts(const int32_t* topk_ids, int32_t num_picks, int32_t num_experts,
+                                   int32_t* counts, void* stream) {
+  if (num_experts < 1 || num_experts > 4096 || num_picks < 0) return BSG_ERR_SHAPE;
+  if ((num_picks > 0 && !topk_ids) || !counts) return BSG_ERR_NULL;
+  if ((topk_ids && !aligned(topk_ids, 4)) || !aligned(counts, 4)) return BSG_ERR_ALIGN;
+  if (int st = check_device()) return st;
+  hipError_t err = bsg::launch_route_counts(topk_ids, num_picks, num_experts, counts,
+                                            static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
+}
+
+extern "C" int bsgemm_quantize_permute(const void* x, uint32_t x_dtype, const int32_t* topk_ids,
+                                       int32_t tokens, int32_t top_k, int32_t K, int32_t num_experts,
+                                       const int32_t* expert_offsets, int32_t M, int32_t* dest,
+                                       void* qa, float* a_scales, void* stream) {
+  if (x_dtype != BSG_OUT_F32 && x_dtype != BSG_OUT_BF16) return BSG_ERR_FMT;
+  if (tokens < 0 || top_k < 1 || K <= 0 || K % 128 || M < 0 || num_experts < 1 ||
+      num_experts > 4096 || (long long)tokens * top_k > INT32_MAX)
+    return BSG_ERR_SHAPE;
+  if (!expert_offsets || (M > 0 && (!qa || !a_scales)) ||
+      (tokens > 0 && (!x || !topk_ids || !dest)))
+    return BSG_ERR_NULL;
+  if ((x && !aligned(x, 16)) || (qa && !aligned(qa, 16)) || (a_scales && !aligned(a_scales, 4)) ||
+      (topk_ids && !aligned(topk_ids, 4)) || (dest && !aligned(dest, 4)) || !aligned(expert_offsets, 4))
+    return BSG_ERR_ALIGN;
+  if (int st = check_device()) return st;
+  hipError_t err = bsg::launch_quantize_permute(x, x_dtype == BSG_OUT_F32 ? 1 : 0, topk_ids, tokens, top_k,
+                                                K, num_experts, expert_offsets, M, dest,
+                                                static_cast<uint8_t*>(qa), a_scales,
+                                                static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
+}
+
 extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B,
                               const void* b_scales, const int32_t* expert_ids,
                               const int32_t* tile_offsets, int32_t num_tiles, void* C, int32_t M,

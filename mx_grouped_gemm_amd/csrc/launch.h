@@ -25,6 +25,15 @@ hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream);
 // MX (e8m0 per 32 K). fmt_a / fmt_b: 1 e4m3, 2 e2m1. out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream);
 
+// Picks per expert (histogram of top-k ids).
+hipError_t launch_route_counts(const int32_t* ids, int n, int E, int32_t* counts, hipStream_t stream);
+
+// Rows of the picks in the grouped A, padding rows, and the e4m3 1x128 quantisation of the
+// token rows into them. x_f32: 1 fp32 activations, 0 bf16.
+hipError_t launch_quantize_permute(const void* x, int x_f32, const int32_t* ids, int tokens, int top_k,
+                                   int K, int E, const int32_t* expert_offsets, int M, int32_t* dest,
+                                   uint8_t* qa, float* a_scales, hipStream_t stream);
+
 // Token-to-expert tile map.
 hipError_t launch_build_tiles(const int32_t* counts, int num_experts, int num_tiles, int padded,
                               int32_t* expert_offsets, int32_t* tile_offsets, int32_t* expert_ids,

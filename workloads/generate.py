@@ -20,6 +20,9 @@ Recipes (all seeded; ``seed`` defaults to 0):
   at most once) with the surplus refilled over the uncapped experts.
 * Grouped layout: experts in ascending order, each group starting at a
   multiple of 128 rows; padding rows are zero with scale 1.
+* Token picks (for the quantise-and-permute step): the routing counts dealt
+  column-wise over ``tokens x top_k`` so each token's experts are distinct,
+  then token and slot order shuffled; activations bf16 from N(0, 1).
 
 Nothing here computes the GEMM or its tile map.
 """
@@ -67,6 +70,30 @@ def routing_counts(tokens, top_k, experts, alpha, n_empty=0, seed=0):
         counts[free] += _largest_remainder(p[free], surplus)
     assert counts.sum() == total
     return counts
+
+
+def routing_topk(counts, tokens, top_k, seed=0):
+    """Top-k picks ``int32 [tokens, top_k]`` (distinct experts per token) whose per-expert
+    totals are ``counts`` (each at most ``tokens``, summing to ``tokens * top_k``).
+
+    The expert ids sorted by expert are dealt column-wise (pick i goes to token i % tokens,
+    slot i // tokens), so one expert's picks land on distinct tokens; token order and the
+    order of each token's slots are then shuffled (seeded)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    if counts.sum() != tokens * top_k or np.any(counts > tokens) or np.any(counts < 0):
+        raise ValueError("counts must sum to tokens * top_k with each count <= tokens")
+    rng = np.random.default_rng(seed + 1)
+    flat = np.repeat(np.arange(len(counts)), counts)
+    ids = flat.reshape(top_k, tokens).T.copy()
+    ids = ids[rng.permutation(tokens)]
+    ids = np.take_along_axis(ids, np.argsort(rng.random(ids.shape), axis=1), axis=1)
+    return ids.astype(np.int32)
+
+
+def activations(tokens, K, device="cpu", seed=0, dtype=torch.bfloat16):
+    """Token activations ~ N(0, 1), ``[tokens, K]`` in ``dtype`` (bf16 by default)."""
+    gen = torch.Generator(device=device).manual_seed(seed + 2)
+    return torch.randn(tokens, K, generator=gen, device=device).to(dtype)
 
 
 def padded_starts(counts, tile=128):
