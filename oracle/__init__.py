@@ -24,6 +24,10 @@ What it computes, and from which passages:
   dequantise both operands, then one fp64 matmul per expert.
 * ``gemm.mx_gemm`` - the MX (e8m0 per 32 K-elements) product, which the Gluon
   page's ``make_problem`` defines as ``A_ref @ B_ref.T`` on dequantised values.
+* ``permute`` - the step before the GEMM: picks per expert, the row of each
+  top-k pick in the padded expert-sorted A (the grouping ``expert_ids`` implies
+  on the "promote_accumulators" page, section Args), and the 1 x 128 e4m3
+  quantisation of token rows with an exact round-to-nearest-even encoder.
 
 Every function works in fp64. Pins: ``tests/test_oracle_*.py`` (exact rational
 brute force, power-of-two scale invariance, grouped == per-expert dense,
