@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--workload", default="moe32",
                     choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
                              "permute_moe32"])
+    ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
+                    help="K of the mx8192_* workloads (M = N = 8192; the pages' K sweep runs "
+                         "512 .. 8192)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB "
                          "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
@@ -122,8 +125,15 @@ def cpu_baseline_mx(p, rows=1024):
 
 
 def bench_mx(args, torch, bsg, make_problem):
-    """A step is one dense MX GEMM launch on a resident 8192^3 problem."""
-    p = make_problem(args.workload, device="cuda", seed=args.seed)
+    """A step is one dense MX GEMM launch on a resident 8192 x 8192 x K problem."""
+    if args.mx_k == 8192:
+        p = make_problem(args.workload, device="cuda", seed=args.seed)
+    else:
+        from workloads.generate import mx_problem
+        if args.mx_k <= 0 or args.mx_k % 128:
+            raise SystemExit("--mx-k must be a positive multiple of 128")
+        fa, fb = args.workload.split("_")[1:]
+        p = mx_problem(8192, 8192, args.mx_k, fa, fb, device="cuda", seed=args.seed)
     C = torch.empty(p.M, p.N, dtype=torch.float16, device="cuda")
     fmt = bsg.make_fmt(p.fmt_a, p.fmt_b, "mx", "f16")
     stream = torch.cuda.current_stream()
@@ -159,8 +169,8 @@ def bench_mx(args, torch, bsg, make_problem):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": f"{p.fmt_a}x{p.fmt_b}", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: dense MX GEMM M=N=K=8192, e8m0 scales per 32 K, "
-                               f"fp16 out", "seed": args.seed},
+        "config": {"workload": f"{args.workload}: dense MX GEMM M=N=8192, K={p.K}, e8m0 scales per "
+                               f"32 K, fp16 out", "K": p.K, "seed": args.seed},
         "kernels_ms": {"mx": round(kernel_ms, 4)},
         "roofline": {
             "kernel": f"mx_kernel<{p.fmt_a}, {p.fmt_b}>", "bound": "mfma",

@@ -284,6 +284,16 @@ def test_mx_grouped():
     check(p, "f16", C, label="mx grouped")
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e2m1")])
+@pytest.mark.parametrize("K", [512, 1024, 2048, 4096])
+def test_mx_k_sweep(fa, fb, K):
+    """The K values of the MX K sweep (at M = N = 1024; the 8192 case is the full-size test)."""
+    p = mx_problem(1024, 1024, K, fa, fb, device="cuda", seed=K + 1)
+    C, _, _ = run_problem(p, "f16")
+    rows = sample_rows(p, per_tile=8, seed=K)
+    check(p, "f16", C, rows=rows, label=f"mx sweep {fa}x{fb} K={K}")
+
+
 @pytest.mark.parametrize("name", ["mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1"])
 def test_mx8192_sampled(name):
     p = make_problem(name, device="cuda")
