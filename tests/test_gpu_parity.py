@@ -82,6 +82,28 @@ def test_dense_k_depths(K):
     check(p, "f32", C, label=f"dense K={K}")
 
 
+def test_output_beyond_4gib():
+    """C of 140000 x 16384 bf16 (4.3 GiB): row offsets past 2^32 bytes (64-bit addressing in the
+    epilogue, per-tile buffer resources for A). Dense rows are independent, so the oracle runs on
+    the sampled rows alone (the last ones included) and is compared with those rows of C."""
+    M, N, K = 140000, 16384, 128
+    p = blockwise_problem(None, N, K, device="cuda", a_rows=M, seed=21)
+    C, _, _ = run_problem(p, "bf16")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 4999), np.arange(M - 300, M)]))
+    idx = torch.from_numpy(rows).cuda()
+    got = C.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    del C
+    torch.cuda.empty_cache()
+    qa, sa = p.qa.index_select(0, idx).cpu().numpy(), p.a_scales.index_select(0, idx).cpu().numpy()
+    qb, sb = p.qb.cpu().numpy(), p.b_scales.cpu().numpy()
+    ref = og.blockwise_grouped(qa, sa, qb, sb)
+    den = og.blockwise_grouped_dequant(qa, sa, qb, sb, absolute=True)
+    err = og.relative_error(got, ref, den)
+    say(f"[parity] dense C > 4 GiB rows={len(rows)} max_rel_err={err:.3e}")
+    assert err <= 8e-3
+
+
 def test_dense_ragged_m_and_n_tail():
     """M not a multiple of 128 (ragged last tile) and N with a half-empty 256-column block."""
     p = blockwise_problem(None, 384, 512, device="cuda", a_rows=200, seed=3)
