@@ -8,7 +8,6 @@ namespace bsg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
@@ -33,15 +32,6 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// Direct global -> LDS copies. The LDS destination is wave-uniform; lane i's bytes land at
-// lds + i * size (global_load_lds_dword / _dwordx4).
-__device__ __forceinline__ void g2lds16(const void* g, lds_void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-__device__ __forceinline__ void g2lds4(const void* g, lds_void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
 __device__ __forceinline__ lds_void* as_lds(uint8_t* p) { return (lds_void*)p; }
@@ -70,12 +60,10 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
   return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// XOR swizzle of 16-byte chunks inside an LDS tile row. With 128-byte rows (8 chunks), chunk c
-// of local row r is stored at slot c ^ swz8(r); 16 consecutive rows read at the same chunk
-// then touch 16 different 16-byte bank groups. With 64-byte rows (4 chunks) the same holds
-// for swz4.
+// XOR swizzle of 16-byte chunks inside an LDS tile row of 128 bytes (8 chunks): chunk c of
+// local row r is stored at slot c ^ swz8(r); 16 consecutive rows read at the same chunk then
+// touch 16 different 16-byte bank groups.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 // Output conversions (round to nearest even).
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
