@@ -21,6 +21,11 @@ counts of the top-8 picks, the tile map, and the permutation of the 16384 bf16 t
 (K = 7168) into the padded expert-sorted A with e4m3 1x128 quantisation. It is HBM-bound: the
 value is GB/s of algorithmic bytes and the roofline is against the 8 TB/s HBM peak.
 
+With --workload decode_moe32 a step is the gate_up GEMM (N=4096, K=7168, 32 experts) for a
+decode batch of 128 tokens x top-8 (about 34 rows per expert), with the schedule for M-tiles of
+few rows (fmt | SCHED_SMALL_M). Streaming B bounds it: GB/s of algorithmic bytes against the
+HBM peak; the large-tile schedule is timed beside it.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload W]
        python bench.py --copy-calibration MIB --steps K   (HBM counter calibration)
 """
@@ -64,7 +69,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="moe32",
                     choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
-                             "permute_moe32"])
+                             "permute_moe32", "decode_moe32"])
     ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
                     help="K of the mx8192_* workloads (M = N = 8192; the pages' K sweep runs "
                          "512 .. 8192)")
@@ -281,6 +286,92 @@ def bench_permute(args, torch, bsg):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, torch, bsg):
+    """A step: the gate_up grouped GEMM of a 128-token decode batch, small-M schedule."""
+    from workloads.generate import blockwise_problem, routing_counts
+
+    route = dict(tokens=128, top_k=8, experts=32, alpha=1.0, n_empty=2)
+    counts = routing_counts(seed=args.seed, **route)
+    N, K, E = 4096, 7168, 32
+    p = blockwise_problem(list(int(c) for c in counts), N, K, device="cuda", seed=args.seed)
+    c = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    T = p.M // 128
+    _, to, ei = bsg.bsgemm_build_tiles(c, T, padded=True)
+    C = torch.empty(p.M, N, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    active = int(np.count_nonzero(counts))
+    real = int(np.sum(counts))
+    nbytes = (active * N * K + active * (N // 128) * (K // 128) * 4      # B and its scales
+              + p.M * K + p.M * (K // 128) * 4 + real * N * 2)            # A, a_scales, C rows
+
+    def time_fmt(small, steps, warmup):
+        fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16", small_m=small)
+        call = lambda: bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei, to, C, p.M, N, K,
+                                          fmt, num_experts=E, stream=stream)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return wall, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    large_wall, large_ms = time_fmt(False, args.steps, args.warmup)
+    ms_per_step, call_ms = time_fmt(True, args.steps, args.warmup)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "GB/s, grouped blockwise-FP8 GEMM for a decode batch (B streamed once per expert)",
+        "value": round(value, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": f"decode_moe32: 128 tokens x top-8 over 32 experts (Dirichlet(1.0), "
+                               f"2 empty) = {real} rows in {T} M-tiles; gate_up N={N}, K={K}; bf16 out",
+                   "tokens": 128, "top_k": 8, "experts": E, "rows": real, "m_tiles": T, "seed": args.seed},
+        "kernels_ms": {"small_m_schedule": round(call_ms, 4), "large_tile_schedule": round(large_ms, 4)},
+        "useful_tflops": round(2.0 * real * N * K / (call_ms * 1e-3) / 1e12, 1),
+        "roofline": {
+            "kernel": "bw_fp8_small_m_kernel (gate_up, decode batch)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(p, counts, ei, to, nbytes)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(p, counts, ei, to, nbytes, n_experts=4):
+    """Time the oracle on the rows of the first ``n_experts`` non-empty experts; report GB/s of
+    the same byte accounting scaled by the share of rows."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as og
+
+    eo, to_r, ei_r = og.tile_map(counts, p.M // 128)
+    live = [e for e in range(len(counts)) if counts[e] > 0][:n_experts]
+    rows = np.concatenate([np.arange(eo[e], eo[e] + counts[e]) for e in live])
+    args = [t.cpu().numpy() for t in (p.qa, p.a_scales, p.qb, p.b_scales)]
+    t0 = time.perf_counter()
+    og.blockwise_grouped(*args, ei_r, to_r, rows=rows)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    share = len(live) / max(1, int(np.count_nonzero(counts)))
+    return {
+        "value": nbytes * share / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"rows of the first {len(live)} non-empty experts ({len(rows)} rows), fp64 oracle "
+                  f"K block by K block; {dt:.1f} s",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,6 +403,9 @@ def main():
 
     if args.workload == "permute_moe32":
         bench_permute(args, torch, bsg)
+        return
+    if args.workload == "decode_moe32":
+        bench_decode(args, torch, bsg)
         return
     if args.workload != "moe32":
         bench_mx(args, torch, bsg, make_problem)

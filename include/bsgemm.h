@@ -51,6 +51,11 @@ typedef enum {
 #define BSG_OUT_F16 3u
 #define BSG_FMT(a_elem, b_elem, scale, out) \
   ((uint32_t)(a_elem) | ((uint32_t)(b_elem) << 4) | ((uint32_t)(scale) << 8) | ((uint32_t)(out) << 12))
+/* Schedule hint (OR into fmt; blockwise only): M-tiles hold few rows (decode-sized expert
+ * groups). Each work item is then one M-tile x 256 columns with the tile's rows taken 32 at a
+ * time, instead of a 256 x 256 block tile. Same results, bit for bit (same instruction, operand
+ * roles and promotion order); faster when most tiles hold well under 128 rows. */
+#define BSG_SCHED_SMALL_M (1u << 16)
 
 /*
  * bsgemm_build_tiles - token-to-expert tile map (the scheduler build).
@@ -110,8 +115,8 @@ int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_t
  *              rows no tile covers are not written.
  * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0, both multiples of 128; num_experts >= 1;
  *   num_tiles >= 0.
- * Supported fmt: blockwise with A = B = e4m3, any output type; MX with A, B in {e4m3, e2m1},
- *   any output type.
+ * Supported fmt: blockwise with A = B = e4m3, any output type (optionally | BSG_SCHED_SMALL_M);
+ *   MX with A, B in {e4m3, e2m1}, any output type.
  * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN, BSG_ERR_FMT, BSG_ERR_DEVICE,
  *   BSG_ERR_LAUNCH.
  */

@@ -66,9 +66,14 @@ def bsgemm_status_string(status):
     return load_library().bsgemm_status_string(int(status)).decode()
 
 
-def make_fmt(a_elem, b_elem, scale, out):
-    """Pack element formats, scale kind and output type into the C ABI's ``fmt`` word."""
-    return ELEM[a_elem] | (ELEM[b_elem] << 4) | (SCALE[scale] << 8) | (OUT[out] << 12)
+SCHED_SMALL_M = 1 << 16
+
+
+def make_fmt(a_elem, b_elem, scale, out, small_m=False):
+    """Pack element formats, scale kind and output type into the C ABI's ``fmt`` word
+    (``small_m``: the schedule for M-tiles of few rows, blockwise only)."""
+    return (ELEM[a_elem] | (ELEM[b_elem] << 4) | (SCALE[scale] << 8) | (OUT[out] << 12)
+            | (SCHED_SMALL_M if small_m else 0))
 
 
 def _ptr(t):

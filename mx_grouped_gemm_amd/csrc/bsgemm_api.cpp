@@ -108,7 +108,9 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
                               int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
                               void* stream) {
   const unsigned fa = fmt & 0xF, fb = (fmt >> 4) & 0xF, sk = (fmt >> 8) & 0xF, out = (fmt >> 12) & 0xF;
-  if ((fmt >> 16) != 0 || out < BSG_OUT_F32 || out > BSG_OUT_F16) return BSG_ERR_FMT;
+  const unsigned hint = fmt >> 16;
+  if (hint > 1 || out < BSG_OUT_F32 || out > BSG_OUT_F16) return BSG_ERR_FMT;
+  if (hint && sk != BSG_SCALE_BLOCKWISE) return BSG_ERR_FMT;
   if (sk == BSG_SCALE_BLOCKWISE) {
     if (fa != BSG_ELEM_E4M3 || fb != BSG_ELEM_E4M3) return BSG_ERR_FMT;
   } else if (sk == BSG_SCALE_MX) {
@@ -143,7 +145,8 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
   args.num_tiles = dense ? (M + 127) / 128 : num_tiles;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = sk == BSG_SCALE_BLOCKWISE
-                       ? bsg::launch_blockwise_fp8(args, static_cast<int>(out), s)
+                       ? (hint ? bsg::launch_blockwise_fp8_small_m(args, static_cast<int>(out), s)
+                               : bsg::launch_blockwise_fp8(args, static_cast<int>(out), s))
                        : bsg::launch_mx(args, static_cast<int>(fa), static_cast<int>(fb),
                                         static_cast<int>(out), s);
   return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;

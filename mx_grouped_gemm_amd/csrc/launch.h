@@ -22,6 +22,9 @@ struct GemmArgs {
 // Blockwise-FP8 (e4m3 x e4m3, fp32 1x128 / 128x128 scales). out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream);
 
+// Blockwise-FP8 scheduled for M-tiles of few rows: one work item per M-tile x 256 columns.
+hipError_t launch_blockwise_fp8_small_m(const GemmArgs& a, int out, hipStream_t stream);
+
 // MX (e8m0 per 32 K). fmt_a / fmt_b: 1 e4m3, 2 e2m1. out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream);
 

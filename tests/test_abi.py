@@ -87,3 +87,11 @@ def test_build_tiles_validation():
     assert lib.bsgemm_build_tiles(None, 4, 4, 1, P16, P16, P16, None) == -1
     assert lib.bsgemm_build_tiles(P16, 4, 4, 1, P16, P16, None, None) == -1
     assert lib.bsgemm_build_tiles(ODD, 4, 4, 1, P16, P16, P16, None) == -3
+
+
+def test_schedule_hint_validation():
+    """The small-M schedule hint is accepted for blockwise only; other hint bits are rejected."""
+    mx = bsg.make_fmt("e4m3", "e4m3", "mx", "f16")
+    assert grouped(fmt=mx | bsg.SCHED_SMALL_M) == -4
+    assert grouped(fmt=bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16") | (2 << 16)) == -4
+

@@ -324,3 +324,56 @@ def test_mx8192_sampled(name):
     assert bool(torch.isfinite(C).all())
     rows = sample_rows(p, per_tile=2)
     check(p, "f16", C, rows=rows, label=name)
+
+
+# --------------------------------------------------------------------------------------
+# schedule for M-tiles of few rows (fmt | SCHED_SMALL_M)
+# --------------------------------------------------------------------------------------
+def _grouped_inputs(counts, N, K, padded, seed):
+    from workloads.generate import quantize_e4m3_rowblocks, quantize_e4m3_tiles
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    total = sum(counts) if not padded else sum(-(-c // 128) * 128 for c in counts)
+    E = len(counts)
+    qa, sa = quantize_e4m3_rowblocks(torch.randn(total, K, generator=gen, device="cuda"))
+    qb, sb = quantize_e4m3_tiles(torch.randn(E, N, K, generator=gen, device="cuda"))
+    T = int(sum(-(-c // 128) for c in counts))
+    _, to, ei = gpu_tile_map(counts, T, padded=padded)
+    return qa, sa, qb, sb, to, ei, total, T
+
+
+@pytest.mark.parametrize("padded,K,out", [(False, 128, "bf16"), (False, 256, "f32"), (True, 384, "f16"),
+                                          (False, 640, "bf16"), (True, 1152, "f32")])
+def test_small_m_schedule_matches(padded, K, out):
+    """Decode-sized groups (1..128 rows, one empty): the small-M schedule equals the large-tile
+    kernel bit for bit and the oracle within tolerance; K from one block (fewer blocks than
+    ring stages) up; rows outside the groups stay untouched."""
+    counts = [1, 5, 0, 17, 32, 33, 64, 100, 128, 3]
+    N = 384
+    qa, sa, qb, sb, to, ei, total, T = _grouped_inputs(counts, N, K, padded, seed=K)
+    E = len(counts)
+    outs = []
+    for small in (False, True):
+        C = poisoned(total, N, out)
+        bsg.bsgemm_grouped(qa, sa, qb, sb, ei, to, C, total, N, K,
+                           bsg.make_fmt("e4m3", "e4m3", "blockwise", out, small_m=small), num_experts=E)
+        outs.append(C)
+    torch.cuda.synchronize()
+    a, b = (c.view(torch.int32 if out == "f32" else torch.int16) for c in outs)
+    assert torch.equal(a, b), "small-M schedule differs from the large-tile kernel"
+
+    class P:
+        pass
+    p = P()
+    p.qa, p.a_scales, p.qb, p.b_scales = qa, sa, qb, sb
+    p.scale_kind, p.fmt_a, p.fmt_b, p.M, p.N, p.K, p.counts = "blockwise", "e4m3", "e4m3", total, N, K, None
+    _, to_r, ei_r = og.tile_map(counts, T, padded=padded)
+    check(p, out, outs[1], tile_map_ref=(ei_r, to_r), label=f"small-M padded={padded} K={K}")
+
+
+def test_small_m_schedule_dense_ragged():
+    p = blockwise_problem(None, 512, 512, device="cuda", a_rows=200, seed=5)
+    C = poisoned(p.M, p.N, "bf16")
+    bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C, p.M, p.N, p.K,
+                       bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16", small_m=True))
+    check(p, "bf16", C, label="small-M dense M=200")
+
