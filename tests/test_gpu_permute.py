@@ -106,3 +106,16 @@ def test_moe32_full_size_sampled():
         lo, hi = eo_ref[e] + counts[e], eo_ref[e + 1]
         assert not np.any(qa[lo:hi]) and np.all(sa[lo:hi] == 1.0)
     say(f"[permute] moe32 full size: {len(toks)} tokens x {k} rows and all padding rows match")
+
+
+@pytest.mark.parametrize("T,k,E,K,dtype", [(97, 10, 16, 128, torch.float32),
+                                            (64, 3, 4096, 256, torch.bfloat16)])
+def test_edge_shapes(T, k, E, K, dtype):
+    """top_k above 8 (the quantiser's destinations come in groups of 8), one K block, and the
+    largest expert count (a 16 KiB LDS histogram); most of the 4096 experts stay empty."""
+    rng = np.random.default_rng(T + k)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(dtype)
+    counts = op.route_counts(ids, E)
+    T_tiles = int(sum(-(-c // 128) for c in counts))
+    _check(x, ids, E, T_tiles, f"edge T={T} k={k} E={E} K={K}")
