@@ -24,6 +24,8 @@ What it computes, and from which passages:
   dequantise both operands, then one fp64 matmul per expert.
 * ``gemm.mx_gemm`` - the MX (e8m0 per 32 K-elements) product, which the Gluon
   page's ``make_problem`` defines as ``A_ref @ B_ref.T`` on dequantised values.
+* ``gemm.nv_gemm`` - the nvfp4 product of the same page (e2m1 elements, one
+  ``float8_e4m3fn`` scale per 16 K-elements), again ``A_ref @ B_ref.T``.
 * ``permute`` - the step before the GEMM: picks per expert, the row of each
   top-k pick in the padded expert-sorted A (the grouping ``expert_ids`` implies
   on the "promote_accumulators" page, section Args), and the 1 x 128 e4m3

@@ -27,15 +27,21 @@ MX variant (Triton Gluon page "Overlapping Accumulator Block-Scaled Matrix
 Multiplication", ``make_problem`` and ``random_quantized_tensor``): every 32
 consecutive K elements of a row of A (of B) share one e8m0 scale, and the
 result is ``A_ref @ B_ref.T`` on the dequantised values.
+
+nvfp4 variant (same page, the ``nvfp4`` format of ``random_quantized_tensor``):
+e2m1 elements packed two per byte along K, and one ``float8_e4m3fn`` scale per
+16 consecutive K elements of a row (``VEC_SIZE = 16``); the result is again
+``A_ref @ B_ref.T`` with ``X_ref = e2m1 * scale.repeat_interleave(16)``.
 """
 
 import numpy as np
 
-from .formats import decode_e8m0, decode_elements
+from .formats import decode_e4m3fn, decode_e8m0, decode_elements
 
 TILE_M = 128      # rows per M-tile of the token-to-expert map
 SCALE_BLOCK = 128  # blockwise scale granularity along N (B) and K (A and B)
 MX_BLOCK = 32      # K elements per e8m0 scale
+NV_BLOCK = 16      # K elements per e4m3 scale (nvfp4)
 
 
 # --------------------------------------------------------------------------------------
@@ -234,6 +240,38 @@ def mx_gemm(qa, a_scales, qb, b_scales, fmt_a, fmt_b, expert_ids=None, tile_offs
 
     return _grouped_dequant(lambda r: dequantize_mx(qa[r], a_scales[r], fmt_a),
                             deq_b, N, expert_ids, tile_offsets, M, rows, absolute)
+
+
+# --------------------------------------------------------------------------------------
+# f4: nvfp4 GEMM (e2m1 elements, an e4m3 scale per 16 K-elements)
+# --------------------------------------------------------------------------------------
+def dequantize_nv(q, scales):
+    """``e2m1(q)[r, k] * e4m3(scales[r, k // 16])`` in fp64 (``q`` packed ``[..., K/2]``)."""
+    v = decode_elements(q, "e2m1")
+    return v * np.repeat(decode_e4m3fn(scales), NV_BLOCK, axis=-1)
+
+
+def nv_gemm(qa, a_scales, qb, b_scales, expert_ids=None, tile_offsets=None, rows=None,
+            absolute=False):
+    """nvfp4 product ``A_ref @ B_ref^T`` on the dequantised values (Gluon page,
+    ``random_quantized_tensor`` for ``nvfp4`` and the reference of ``make_problem``).
+
+    ``qa``: packed e2m1 ``[M, K/2]``; ``a_scales`` uint8 e4m3 ``[M, K/16]``.
+    ``qb``: ``[E, N, K/2]`` (or ``[N, K/2]``); ``b_scales`` uint8 ``[E, N, K/16]``
+    (or ``[N, K/16]``). Grouping as in :func:`blockwise_grouped`.
+    """
+    qa = np.asarray(qa, np.uint8)
+    a_scales = np.asarray(a_scales, np.uint8)
+    b_scales = np.asarray(b_scales, np.uint8)
+    M = qa.shape[0]
+    N = np.asarray(qb).shape[-2]
+
+    def deq_b(e):
+        sb = b_scales if b_scales.ndim == 2 else b_scales[e]
+        return dequantize_nv(_expert_b(qb, e), sb)
+
+    return _grouped_dequant(lambda r: dequantize_nv(qa[r], a_scales[r]), deq_b, N, expert_ids,
+                            tile_offsets, M, rows, absolute)
 
 
 # --------------------------------------------------------------------------------------

@@ -18,9 +18,10 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import formats as ofmt
 from oracle import gemm as og
 from tests.conftest import read_golden
-from workloads.generate import blockwise_problem, mx_problem
+from workloads.generate import blockwise_problem, mx_problem, nv_problem
 
 NAN_CODES = (0x7F, 0xFF)
 
@@ -378,6 +379,131 @@ def test_mx_unit_scales_equal_blockwise_unit_scales():
                     "e4m3", "e4m3")
     bw = og.blockwise_grouped(qa, np.ones((8, 2), np.float32), qb, np.ones((1, 2), np.float32))
     assert np.array_equal(mx, bw)
+
+
+# --------------------------------------------------------------------------------------
+# nvfp4 (e2m1 elements, e4m3 scale per 16 K)
+# --------------------------------------------------------------------------------------
+def exact_nv(qa, sa, qb, sb):
+    """Exact Fractions: element ints from the golden e2m1 table, scales via torch's e4m3."""
+    ia, ib = spec_e2m1_int(qa), spec_e2m1_int(qb)             # value * 2
+    ja, jb = lib_e4m3_int(sa), lib_e4m3_int(sb)               # scale * 512
+    M, K = ia.shape
+    N = ib.shape[0]
+    out = np.empty((M, N), object)
+    for m in range(M):
+        for n in range(N):
+            t = 0
+            for j in range(K // 16):
+                k = slice(16 * j, 16 * j + 16)
+                t += int(np.dot(ia[m, k], ib[n, k])) * int(ja[m, j]) * int(jb[n, j])
+            out[m, n] = Fraction(t, 2 * 2 * 512 * 512)
+    return out
+
+
+def random_nv(rng, M, N, K, signed_scales=True):
+    qa = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    qb = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sa, sb = random_codes(rng, (M, K // 16)), random_codes(rng, (N, K // 16))
+    if not signed_scales:
+        sa, sb = sa & 0x7F, sb & 0x7F
+    return qa, sa, qb, sb
+
+
+def test_nv_matches_exact():
+    """Every e2m1 byte and every finite e4m3 scale code (subnormal, negative and 448 included):
+    with K = 128 each sum is exact in fp64, so the oracle must equal the rational result."""
+    rng = np.random.default_rng(21)
+    qa, sa, qb, sb = random_nv(rng, 6, 8, 128)
+    C = og.nv_gemm(qa, sa, qb, sb)
+    want = exact_nv(qa, sa, qb, sb)
+    for m in range(6):
+        for n in range(8):
+            assert C[m, n] == float(want[m, n])
+
+
+def _nv_mutant(bug):
+    def deq(q, s, side="b"):
+        codes = ofmt.unpack_e2m1(q)
+        if bug == "nibble_order" and side == "a":   # on both operands it would cancel
+            codes = codes.reshape(codes.shape[:-1] + (-1, 2))[..., ::-1].reshape(codes.shape)
+        v = ofmt.decode_e2m1(codes)
+        if bug == "scale_block_32":
+            sc = np.repeat(ofmt.decode_e4m3fn(s), 32, axis=-1)[..., :v.shape[-1]]
+        elif bug == "e8m0_scales":
+            sc = np.repeat(ofmt.decode_e8m0(s), 16, axis=-1)
+        else:
+            sc = np.repeat(ofmt.decode_e4m3fn(s), 16, axis=-1)
+        return v * sc
+
+    def fn(qa, sa, qb, sb):
+        a, b = deq(qa, sa, "a"), deq(qb, sb)
+        if bug == "scales_swapped":
+            a, b = deq(qa, sb[: qa.shape[0]]), deq(qb, sa[: qb.shape[0]])
+        return a @ b.T
+
+    return fn
+
+
+@pytest.mark.parametrize("bug", ["nibble_order", "scale_block_32", "e8m0_scales", "scales_swapped"])
+def test_nv_planted_mistakes_are_caught(bug):
+    rng = np.random.default_rng(22)
+    qa, sa, qb, sb = random_nv(rng, 6, 6, 128, signed_scales=False)
+    want = exact_nv(qa, sa, qb, sb)
+    got = _nv_mutant(bug)(qa, sa, qb, sb)
+    assert any(got[m, n] != float(want[m, n]) for m in range(6) for n in range(6))
+
+
+def test_nv_power_of_two_scales_equal_mx():
+    """Scales that are powers of two and equal over each 32 K-elements: the nvfp4 product must
+    equal the MX product with the matching e8m0 codes (a different scale decoder)."""
+    rng = np.random.default_rng(23)
+    M, N, K = 8, 128, 256
+    qa = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    qb = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ea = rng.integers(-9, 9, size=(M, K // 32))
+    eb = rng.integers(-9, 9, size=(N, K // 32))
+    # e4m3 code of 2**e: normal (exponent field e + 7) for e >= -6, else subnormal 2**(e+9) * 2**-9
+    def e4m3_pow2(e):
+        return np.where(e >= -6, (e + 7) << 3, 1 << (e + 9)).astype(np.uint8)
+    nv = og.nv_gemm(qa, np.repeat(e4m3_pow2(ea), 2, axis=1), qb, np.repeat(e4m3_pow2(eb), 2, axis=1))
+    mx = og.mx_gemm(qa, (ea + 127).astype(np.uint8), qb, (eb + 127).astype(np.uint8), "e2m1", "e2m1")
+    assert np.array_equal(nv, mx)
+
+
+def test_nv_scale_code_shift():
+    """Adding 8 to a normal e4m3 code raises its exponent by one: C doubles exactly."""
+    p = nv_problem(8, 128, 256, seed=5)
+    qa, sa, qb, sb = (t.numpy() for t in (p.qa, p.a_scales, p.qb, p.b_scales))
+    assert np.all((sa >> 3) & 0xF >= 1) and np.all((sa >> 3) & 0xF <= 13)
+    base = og.nv_gemm(qa, sa, qb[0], sb[0])
+    assert np.array_equal(og.nv_gemm(qa, sa + 8, qb[0], sb[0]), base * 2.0)
+
+
+def test_nv_grouped_equals_per_expert_dense():
+    p = nv_problem(0, 128, 256, seed=6, counts=[5, 0, 131, 40])
+    qa, sa, qb, sb = (t.numpy() for t in (p.qa, p.a_scales, p.qb, p.b_scales))
+    _, to, ei = og.tile_map(p.counts, p.M // 128)
+    C = og.nv_gemm(qa, sa, qb, sb, ei, to)
+    owner = og.row_experts(ei, to, p.M)
+    for e in range(4):
+        r = np.nonzero(owner == e)[0]
+        if len(r):
+            assert np.array_equal(C[r], og.nv_gemm(qa[r], sa[r], qb[e], sb[e]))
+    assert np.all(np.isnan(C[owner < 0]))
+
+
+def test_nv_quantiser_round_trip_bound():
+    """The input encoder keeps every element within half an e2m1 step (times the scale)."""
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(16, 256, generator=g)
+    from workloads.generate import quantize_nvfp4
+    q, s = quantize_nvfp4(x)
+    deq = og.dequantize_nv(q.numpy(), s.numpy())
+    sc = np.repeat(ofmt.decode_e4m3fn(s.numpy()), 16, axis=-1)
+    xs = np.abs(x.numpy() / sc)
+    step = np.where(xs < 2, 0.5, np.where(xs < 4, 1.0, 2.0))
+    assert np.all(np.abs(deq - x.numpy()) <= (step / 2 + 1e-6) * sc + np.maximum(xs - 6, 0) * sc)
 
 
 # --------------------------------------------------------------------------------------

@@ -14,6 +14,10 @@ Recipes (all seeded; ``seed`` defaults to 0):
   clamped to [0, 254]; elements ``x * 2**-(code - 127)`` rounded to nearest-even
   and saturated to +-448 (e4m3) or +-6 (e2m1). e2m1 is packed two per byte
   along K, even K index in the low nibble.
+* nvfp4: one e4m3 scale per 16 K-elements, ``e4m3(amax / 6)`` rounded to
+  nearest-even (an all-zero block gets scale 1, a scale that rounds to zero the
+  smallest subnormal); elements ``x / scale`` (fp32) rounded to nearest-even
+  e2m1 and saturated to +-6, packed as for MX.
 * Routing: ``p ~ Dirichlet(alpha)`` over the experts (``n_empty`` of them
   forced to zero and ``p`` renormalised), ``tokens * top_k`` rows split by
   largest remainder, each count capped at ``tokens`` (a token picks an expert
@@ -166,6 +170,20 @@ def quantize_mx(x, fmt):
     return q, code.to(torch.uint8).contiguous()
 
 
+def quantize_nvfp4(x):
+    """fp32 ``[..., R, K]`` -> (packed e2m1 ``[..., R, K/2]``, uint8 e4m3 ``[..., R, K/16]``)."""
+    *lead, K = x.shape
+    xb = x.reshape(*lead, K // 16, 16)
+    amax = xb.abs().amax(dim=-1)
+    code = _to_e4m3_bytes(amax / E2M1_MAX)
+    code = torch.where(amax > 0, code, torch.full_like(code, 0x38))     # 1.0
+    code = torch.where(code == 0, torch.ones_like(code), code)          # smallest subnormal
+    s = code.view(torch.float8_e4m3fn).float()
+    y = (xb / s[..., None]).clamp(-E2M1_MAX, E2M1_MAX)
+    q = pack_e2m1(_e2m1_codes(y).reshape(*lead, K))
+    return q, code.contiguous()
+
+
 # --------------------------------------------------------------------------------------
 # problems
 # --------------------------------------------------------------------------------------
@@ -174,7 +192,8 @@ class Problem:
     """One GEMM instance: quantised operands plus the routing they came from."""
 
     name: str
-    scale_kind: str            # "blockwise" (fp32 1x128 / 128x128) or "mx" (e8m0 per 32)
+    scale_kind: str            # "blockwise" (fp32 1x128 / 128x128), "mx" (e8m0 per 32) or
+                               # "nv" (e4m3 per 16, e2m1 elements)
     fmt_a: str                 # "e4m3" | "e2m1"
     fmt_b: str
     out_dtypes: tuple          # subset of ("f32", "bf16", "f16")
@@ -249,6 +268,28 @@ def _mx_problem(name, M, N, K, fmt_a, fmt_b, device, seed):
                    qb[None].contiguous(), sb[None].contiguous())
 
 
+def _nv_problem(name, M, N, K, device, seed, counts=None, E=1):
+    """nvfp4 operands: one dense group of M rows, or grouped (padded layout) from ``counts``."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    if counts is None:
+        qa, sa = quantize_nvfp4(_randn((M, K), gen, device))
+    else:
+        starts = padded_starts(counts)
+        M = int(starts[-1])
+        qa = torch.zeros((M, K // 2), dtype=torch.uint8, device=device)
+        sa = torch.full((M, K // 16), 0x38, dtype=torch.uint8, device=device)
+        for e, c in enumerate(counts):
+            c = int(c)
+            if c:
+                qa[starts[e]:starts[e] + c], sa[starts[e]:starts[e] + c] = quantize_nvfp4(
+                    _randn((c, K), gen, device))
+        E = len(counts)
+    qb, sb = quantize_nvfp4(_randn((E, N, K), gen, device))
+    return Problem(name, "nv", "e2m1", "e2m1", ("f16",), M, N, K, E,
+                   None if counts is None else np.asarray(counts, np.int64), qa, sa,
+                   qb.contiguous(), sb.contiguous())
+
+
 MOE8 = dict(tokens=4096, top_k=2, experts=8, alpha=0.5, n_empty=0)
 MOE32 = dict(tokens=16384, top_k=8, experts=32, alpha=1.0, n_empty=2)
 
@@ -276,6 +317,8 @@ WORKLOADS = {
                                                       "e4m3", "e2m1", dev, seed),
     "mx8192_e2m1_e2m1": lambda dev, seed: _mx_problem("mx8192_e2m1_e2m1", 8192, 8192, 8192,
                                                       "e2m1", "e2m1", dev, seed),
+    # nvfp4 (e2m1, e4m3 scale per 16 K) 8192^3, fp16 output
+    "nvfp4_8192": lambda dev, seed: _nv_problem("nvfp4_8192", 8192, 8192, 8192, dev, seed),
 }
 
 
@@ -290,6 +333,11 @@ def blockwise_problem(counts, N, K, device="cpu", seed=0, a_rows=None, E=None, o
     E = len(counts) if counts is not None else (E or 1)
     return _blockwise_problem("adhoc", counts, N, K, E, out_dtypes, device, seed,
                               outlier_every=outlier_every, a_rows=a_rows)
+
+
+def nv_problem(M, N, K, device="cpu", seed=0, counts=None):
+    """Ad-hoc nvfp4 problem (tests): dense (M rows) or grouped from ``counts``."""
+    return _nv_problem("adhoc_nv", M, N, K, device, seed, counts=counts)
 
 
 def mx_problem(M, N, K, fmt_a, fmt_b, device="cpu", seed=0):
