@@ -16,6 +16,10 @@ With --workload mx8192_<a>_<b> a step is instead one dense MX GEMM of 8192^3 (e8
 32 K, fp16 out) with formats a x b; its roofline is that launch against the peak of the
 narrower-rate format pair.
 
+With --workload nvfp4_8192 a step is one dense nvfp4 GEMM of 8192^3 (e2m1 elements, an e4m3
+scale per 16 K, fp16 out); the products run on the f16 matrix instruction, so its roofline is
+against the f16 peak.
+
 With --workload permute_moe32 a step is the step before the GEMM on the same routing: per-expert
 counts of the top-8 picks, the tile map, and the permutation of the 16384 bf16 token rows
 (K = 7168) into the padded expert-sorted A with e4m3 1x128 quantisation. It is HBM-bound: the
@@ -44,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5033.0   # MI355X dense FP8 MFMA peak (256 CU x 2.4 GHz x 8192 flop/clk)
 PEAK_FP4_TFLOPS = 10066.0  # MI355X dense MXFP4 MFMA peak (twice the FP8 rate)
+PEAK_FP16_TFLOPS = 2516.6  # MI355X dense FP16 MFMA peak (half the FP8 rate)
 PEAK_HBM_GBS = 8000.0
 METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 
@@ -69,10 +74,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="moe32",
                     choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
-                             "permute_moe32", "decode_moe32"])
+                             "nvfp4_8192", "permute_moe32", "decode_moe32"])
     ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
-                    help="K of the mx8192_* workloads (M = N = 8192; the pages' K sweep runs "
-                         "512 .. 8192)")
+                    help="K of the mx8192_* and nvfp4_8192 workloads (M = N = 8192; the pages' "
+                         "K sweep runs 512 .. 8192)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB "
                          "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
@@ -118,21 +123,34 @@ def cpu_baseline_mx(p, rows=1024):
     qa, sa = p.qa[:rows].cpu().numpy(), p.a_scales[:rows].cpu().numpy()
     qb, sb = p.qb.cpu().numpy(), p.b_scales.cpu().numpy()
     t0 = time.perf_counter()
-    og.mx_gemm(qa, sa, qb, sb, p.fmt_a, p.fmt_b)
+    if p.scale_kind == "nv":
+        og.nv_gemm(qa, sa, qb, sb)
+    else:
+        og.mx_gemm(qa, sa, qb, sb, p.fmt_a, p.fmt_b)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
         "value": 2.0 * rows * p.N * p.K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{rows} rows of A of the {p.M}x{p.N}x{p.K} MX GEMM ({p.fmt_a} x {p.fmt_b}), "
+        "sample": f"{rows} rows of A of the {p.M}x{p.N}x{p.K} {KIND_NAME[p.scale_kind]} GEMM "
+                  f"({p.fmt_a} x {p.fmt_b}), "
                   f"fp64 oracle (decode, then one product); {dt:.1f} s",
     }
 
 
+KIND_NAME = {"mx": "MX", "nv": "nvfp4"}
+
+
 def bench_mx(args, torch, bsg, make_problem):
-    """A step is one dense MX GEMM launch on a resident 8192 x 8192 x K problem."""
+    """A step is one dense MX (or nvfp4) GEMM launch on a resident 8192 x 8192 x K problem."""
+    nv = args.workload == "nvfp4_8192"
     if args.mx_k == 8192:
         p = make_problem(args.workload, device="cuda", seed=args.seed)
+    elif nv:
+        from workloads.generate import nv_problem
+        if args.mx_k <= 0 or args.mx_k % 256:
+            raise SystemExit("--mx-k must be a positive multiple of 256 for nvfp4")
+        p = nv_problem(8192, 8192, args.mx_k, device="cuda", seed=args.seed)
     else:
         from workloads.generate import mx_problem
         if args.mx_k <= 0 or args.mx_k % 128:
@@ -140,7 +158,7 @@ def bench_mx(args, torch, bsg, make_problem):
         fa, fb = args.workload.split("_")[1:]
         p = mx_problem(8192, 8192, args.mx_k, fa, fb, device="cuda", seed=args.seed)
     C = torch.empty(p.M, p.N, dtype=torch.float16, device="cuda")
-    fmt = bsg.make_fmt(p.fmt_a, p.fmt_b, "mx", "f16")
+    fmt = bsg.make_fmt(p.fmt_a, p.fmt_b, p.scale_kind, "f16")
     stream = torch.cuda.current_stream()
     launches = []
 
@@ -165,20 +183,28 @@ def bench_mx(args, torch, bsg, make_problem):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in launches]))
     flops = p.useful_flops
-    peak = PEAK_FP4_TFLOPS if (p.fmt_a, p.fmt_b) == ("e2m1", "e2m1") else PEAK_FP8_TFLOPS
+    if nv:
+        # the products run on the f16 matrix instruction (the e4m3 scales are folded into f16
+        # operands), so the f16 rate is the ceiling
+        peak = PEAK_FP16_TFLOPS
+    else:
+        peak = PEAK_FP4_TFLOPS if (p.fmt_a, p.fmt_b) == ("e2m1", "e2m1") else PEAK_FP8_TFLOPS
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
+    scales = "e4m3 per 16" if nv else "e8m0 per 32"
     out = {
-        "metric": f"TFLOP/s, MX GEMM {p.M}x{p.N}x{p.K} ({p.fmt_a} x {p.fmt_b}, e8m0 per 32)",
+        "metric": f"TFLOP/s, {KIND_NAME[p.scale_kind]} GEMM {p.M}x{p.N}x{p.K} ({p.fmt_a} x {p.fmt_b}, "
+                  f"{scales})",
         "value": round(value, 2), "unit": "TFLOP/s", "pct_of_peak": round(100.0 * value / peak, 2),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": f"{p.fmt_a}x{p.fmt_b}", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: dense MX GEMM M=N=8192, K={p.K}, e8m0 scales per "
-                               f"32 K, fp16 out", "K": p.K, "seed": args.seed},
-        "kernels_ms": {"mx": round(kernel_ms, 4)},
+        "config": {"workload": f"{args.workload}: dense {KIND_NAME[p.scale_kind]} GEMM M=N=8192, "
+                               f"K={p.K}, {scales} K, fp16 out", "K": p.K, "seed": args.seed},
+        "kernels_ms": {"nvfp4" if nv else "mx": round(kernel_ms, 4)},
         "roofline": {
-            "kernel": f"mx_kernel<{p.fmt_a}, {p.fmt_b}>", "bound": "mfma",
+            "kernel": "nv_fp4_kernel (f16 MFMA)" if nv else f"mx_kernel<{p.fmt_a}, {p.fmt_b}>",
+            "bound": "mfma",
             "achieved": round(kernel_tflops, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(kernel_tflops / peak, 4), "traffic": None,
         },

@@ -46,6 +46,7 @@ typedef enum {
 #define BSG_ELEM_E2M1 2u   /* OCP e2m1, two per byte along K, even K index in low nibble  */
 #define BSG_SCALE_BLOCKWISE 1u /* fp32: A per row per 128 K; B per 128 (N) x 128 (K) block */
 #define BSG_SCALE_MX 2u        /* e8m0 (uint8, 2^(x-127)): one per row per 32 K, A and B   */
+#define BSG_SCALE_NV 3u        /* nvfp4: e4m3fn (uint8) scale per row per 16 K, A and B    */
 #define BSG_OUT_F32 1u
 #define BSG_OUT_BF16 2u
 #define BSG_OUT_F16 3u
@@ -100,14 +101,20 @@ int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_t
  * MX (BSG_SCALE_MX; passage: Gluon page, random_quantized_tensor / async_mma_scaled_impl):
  *   C[m,n] = sum_k (qa[m,k] 2^(sa[m,k/32]-127)) (qb[e,n,k] 2^(sb[e,n,k/32]-127)), scales
  *   applied by the gfx950 scaled matrix instruction, fp32 accumulation.
+ * nvfp4 (BSG_SCALE_NV; passage: Gluon page, random_quantized_tensor for "nvfp4", VEC_SIZE 16,
+ *   scales converted to float8_e4m3fn):
+ *   C[m,n] = sum_k (e2m1(qa[m,k]) e4m3(sa[m,k/16])) (e2m1(qb[e,n,k]) e4m3(sb[e,n,k/16])), each
+ *   scaled element formed exactly in f16, fp32 accumulation.
  *
  * Layouts (all row-major, contiguous):
  *   A          DEVICE [M, K] e4m3 bytes, or [M, K/2] packed e2m1. 16-byte aligned.
  *   a_scales   blockwise: DEVICE float[M, K/128];  MX: DEVICE uint8[M, K/32]. 4-byte aligned.
+ *              nvfp4: DEVICE uint8[M, K/16] e4m3fn codes, 16-byte aligned.
  *   B          DEVICE [num_experts, N, K] e4m3 (or [num_experts, N, K/2] e2m1): K contiguous,
  *              i.e. each expert's B is stored N-major ("NT" GEMM). 16-byte aligned.
  *   b_scales   blockwise: DEVICE float[num_experts, N/128, K/128];
  *              MX: DEVICE uint8[num_experts, N, K/32]. 4-byte aligned.
+ *              nvfp4: DEVICE uint8[num_experts, N, K/16] e4m3fn codes, 16-byte aligned.
  *   expert_ids DEVICE int32[num_tiles] and tile_offsets DEVICE int32[num_tiles + 1], as written
  *              by bsgemm_build_tiles (either layout). Both NULL: one dense group, expert 0,
  *              tiles of 128 rows, num_tiles ignored (M need not be a multiple of 128).
@@ -116,7 +123,8 @@ int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_t
  * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0, both multiples of 128; num_experts >= 1;
  *   num_tiles >= 0.
  * Supported fmt: blockwise with A = B = e4m3, any output type (optionally | BSG_SCHED_SMALL_M);
- *   MX with A, B in {e4m3, e2m1}, any output type.
+ *   MX with A, B in {e4m3, e2m1}, any output type;
+ *   nvfp4 with A = B = e2m1 and K a multiple of 256 (else BSG_ERR_SHAPE), any output type.
  * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN, BSG_ERR_FMT, BSG_ERR_DEVICE,
  *   BSG_ERR_LAUNCH.
  */

@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_PKG_DIR, "libbsgemm.so")
 _lib = None
 
 ELEM = {"e4m3": 1, "e2m1": 2}
-SCALE = {"blockwise": 1, "mx": 2}
+SCALE = {"blockwise": 1, "mx": 2, "nv": 3}
 OUT = {"f32": 1, "bf16": 2, "f16": 3}
 OUT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 EXPORTED = ("bsgemm_build_tiles", "bsgemm_grouped", "bsgemm_status_string", "bsgemm_route_counts",

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libbsgemm.so")
 
-SOURCES = ["bsgemm_api.cpp", "tile_map.hip", "bs_fp8_grouped.hip", "mx_scaled.hip", "permute.hip", "bs_fp8_small_m.hip"]
+SOURCES = ["bsgemm_api.cpp", "tile_map.hip", "bs_fp8_grouped.hip", "mx_scaled.hip", "permute.hip", "bs_fp8_small_m.hip",
+           "nv_fp4.hip"]
 
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 # -amdgpu-mfma-vgpr-form: MFMA results go to VGPRs, so the promote FMAs read them directly

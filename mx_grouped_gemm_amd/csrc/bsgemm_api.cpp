@@ -116,16 +116,20 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
   } else if (sk == BSG_SCALE_MX) {
     if ((fa != BSG_ELEM_E4M3 && fa != BSG_ELEM_E2M1) || (fb != BSG_ELEM_E4M3 && fb != BSG_ELEM_E2M1))
       return BSG_ERR_FMT;
+  } else if (sk == BSG_SCALE_NV) {
+    if (fa != BSG_ELEM_E2M1 || fb != BSG_ELEM_E2M1) return BSG_ERR_FMT;
   } else {
     return BSG_ERR_FMT;
   }
   if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || num_experts < 1 || num_tiles < 0)
     return BSG_ERR_SHAPE;
+  if (sk == BSG_SCALE_NV && K % 256) return BSG_ERR_SHAPE;
   const bool dense = expert_ids == nullptr && tile_offsets == nullptr;
   if (!dense && (expert_ids == nullptr || tile_offsets == nullptr)) return BSG_ERR_NULL;
   if (!A || !a_scales || !B || !b_scales || !C) return BSG_ERR_NULL;
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scales, 4) ||
-      !aligned(b_scales, 4) || (!dense && (!aligned(expert_ids, 4) || !aligned(tile_offsets, 4))))
+  const uintptr_t scale_align = sk == BSG_SCALE_NV ? 16 : 4;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scales, scale_align) ||
+      !aligned(b_scales, scale_align) || (!dense && (!aligned(expert_ids, 4) || !aligned(tile_offsets, 4))))
     return BSG_ERR_ALIGN;
   if (M == 0 || (!dense && num_tiles == 0)) return BSG_OK;
   if (int st = check_device()) return st;
@@ -144,10 +148,13 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
   args.num_experts = dense ? 1 : num_experts;
   args.num_tiles = dense ? (M + 127) / 128 : num_tiles;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = sk == BSG_SCALE_BLOCKWISE
-                       ? (hint ? bsg::launch_blockwise_fp8_small_m(args, static_cast<int>(out), s)
-                               : bsg::launch_blockwise_fp8(args, static_cast<int>(out), s))
-                       : bsg::launch_mx(args, static_cast<int>(fa), static_cast<int>(fb),
-                                        static_cast<int>(out), s);
+  hipError_t err;
+  if (sk == BSG_SCALE_BLOCKWISE)
+    err = hint ? bsg::launch_blockwise_fp8_small_m(args, static_cast<int>(out), s)
+               : bsg::launch_blockwise_fp8(args, static_cast<int>(out), s);
+  else if (sk == BSG_SCALE_MX)
+    err = bsg::launch_mx(args, static_cast<int>(fa), static_cast<int>(fb), static_cast<int>(out), s);
+  else
+    err = bsg::launch_nvfp4(args, static_cast<int>(out), s);
   return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
 }

@@ -28,6 +28,9 @@ hipError_t launch_blockwise_fp8_small_m(const GemmArgs& a, int out, hipStream_t 
 // MX (e8m0 per 32 K). fmt_a / fmt_b: 1 e4m3, 2 e2m1. out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream);
 
+// nvfp4 (e2m1 x e2m1, e4m3 scale per 16 K; K a multiple of 256). out: 1 f32, 2 bf16, 3 f16.
+hipError_t launch_nvfp4(const GemmArgs& a, int out, hipStream_t stream);
+
 // Picks per expert (histogram of top-k ids).
 hipError_t launch_route_counts(const int32_t* ids, int n, int E, int32_t* counts, hipStream_t stream);
 

@@ -54,6 +54,9 @@ def oracle_reference(prob, expert_ids, tile_offsets, rows=None):
         ref = og.blockwise_grouped(qa, sa, qb, sb, expert_ids, tile_offsets, rows=rows)
         den = og.blockwise_grouped_dequant(qa, sa, qb, sb, expert_ids, tile_offsets, rows=rows,
                                            absolute=True)
+    elif prob.scale_kind == "nv":
+        ref = og.nv_gemm(qa, sa, qb, sb, expert_ids, tile_offsets, rows=rows)
+        den = og.nv_gemm(qa, sa, qb, sb, expert_ids, tile_offsets, rows=rows, absolute=True)
     else:
         ref = og.mx_gemm(qa, sa, qb, sb, prob.fmt_a, prob.fmt_b, expert_ids, tile_offsets, rows=rows)
         den = og.mx_gemm(qa, sa, qb, sb, prob.fmt_a, prob.fmt_b, expert_ids, tile_offsets, rows=rows,

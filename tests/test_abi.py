@@ -95,3 +95,15 @@ def test_schedule_hint_validation():
     assert grouped(fmt=mx | bsg.SCHED_SMALL_M) == -4
     assert grouped(fmt=bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16") | (2 << 16)) == -4
 
+
+
+def test_nvfp4_validation():
+    """nvfp4 takes e2m1 x e2m1 only, K a multiple of 256 and 16-byte aligned scale bases."""
+    nv = bsg.make_fmt("e2m1", "e2m1", "nv", "f16")
+    assert grouped(fmt=bsg.make_fmt("e4m3", "e2m1", "nv", "f16")) == -4
+    assert grouped(fmt=bsg.make_fmt("e2m1", "e4m3", "nv", "f16")) == -4
+    assert grouped(fmt=nv | bsg.SCHED_SMALL_M) == -4
+    assert grouped(fmt=nv, K=384) == -2
+    assert grouped(fmt=nv, sa=P4) == -3
+    assert grouped(fmt=nv, sb=P4) == -3
+    assert grouped(fmt=nv, M=0) == 0
