@@ -22,14 +22,16 @@ SOURCES = ["bsgemm_api.cpp", "tile_map.hip", "bs_fp8_grouped.hip", "mx_scaled.hi
 
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 # -amdgpu-mfma-vgpr-form: MFMA results go to VGPRs, so the promote FMAs read them directly
-#   instead of copying them out of AGPRs first.
+#   instead of copying them out of AGPRs first. Not for the nvfp4 kernel: no VALU reads its
+#   accumulators inside the K loop, and they need the AGPRs (256 per lane, one wave per SIMD).
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"),
 ]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC_SOURCES = {"nv_fp4.hip"}
 
 
 def _hipcc():
@@ -58,7 +60,8 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = [] if src in AGPR_ACC_SOURCES else VGPR_FORM
+        cmds.append([hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

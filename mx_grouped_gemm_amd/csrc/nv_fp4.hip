@@ -12,7 +12,10 @@
 // through v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 //
 // Block structure: 256 x 256 block tiles (super-tiles of two 128-row M-tiles of one expert, as in
-// the other kernels), 8 waves of 64 x 128 as 4 x 8 fragments of 16 x 16, a 2-stage LDS ring of
+// the other kernels), 4 waves (one per SIMD) of 128 x 128 as 8 x 8 fragments of 16 x 16, fp32
+// accumulators in AGPRs. The conversions are VALU work in proportion to the wave tile's rows plus
+// columns, and they, not the matrix unit, bound this kernel: 128 x 128 needs a third fewer per
+// product than 64 x 128 (8 waves, two per SIMD measured 0.50 of the f16 peak). A 2-stage LDS ring of
 // 256-K stages filled by buffer -> LDS copies (stage b+1 is copied while stage b is computed),
 // one barrier per stage. A stage row is 128 bytes of codes and 16 bytes of scales.
 //
@@ -22,8 +25,6 @@
 // and for step s (0..3) of that half its dword s, i.e. K elements [64 q + 32 h + 8 s, + 8). Those
 // 8 elements share the scale of 16-block 4 q + 2 h + s / 2, and the lane's four scale blocks are
 // the dword q of the row's 16 scale bytes.
-#include <type_traits>
-
 #include "common.h"
 #include "launch.h"
 
@@ -38,27 +39,27 @@ constexpr int BM = 256, BN = 256, TILE_M = 128;
 constexpr int KSTAGE = 256;                        // K elements per stage
 constexpr int ROWB = KSTAGE / 2;                   // 128 bytes of e2m1 codes per row and stage
 constexpr int SROWB = KSTAGE / 16;                 // 16 scale bytes per row and stage
-constexpr int NWAVES = 8, NTHREADS = NWAVES * kWave;
-constexpr int WM = 64, WN = 128;                   // wave tile
-constexpr int MI = WM / 16, NJ = WN / 16;          // 4 x 8 fragments of 16 x 16
+constexpr int NWAVES = 4, NTHREADS = NWAVES * kWave;
+constexpr int WM = 128, WN = 128;                  // wave tile (one wave per SIMD)
+constexpr int MI = WM / 16, NJ = WN / 16;          // 8 x 8 fragments of 16 x 16
 constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;        // 32 KiB each
 constexpr int SA_BYTES = BM * SROWB, SB_BYTES = BN * SROWB;    // 4 KiB each
 constexpr int A_OFF = 0, B_OFF = A_BYTES, SA_OFF = B_OFF + B_BYTES, SB_OFF = SA_OFF + SA_BYTES;
 constexpr int STAGE_BYTES = SB_OFF + SB_BYTES;                  // 72 KiB
 constexpr int LDS_BYTES = 2 * STAGE_BYTES;                      // 144 KiB of 160
-constexpr int D_INSTR = A_BYTES / 1024 / NWAVES;                // 4 copies of 1 KiB per operand
+constexpr int D_INSTR = A_BYTES / 1024 / NWAVES;                // 8 copies of 1 KiB per operand
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-static_assert(SA_BYTES == 4 * 1024 && NWAVES == 8, "scale copies: one 1 KiB copy per wave");
+static_assert(SA_BYTES == 4 * 1024 && NWAVES == 4, "scale copies: 1 KiB of A and of B per wave");
 
 struct NvLoadPlan {
-  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, s_rsrc;  // s_rsrc: A scales (waves 0-3) or B (4-7)
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
   uint32_t voff[D_INSTR];  // data copies: per-lane offset of copy i (rows and swizzled chunk)
-  uint32_t s_voff;         // scale copy: this lane's row
-  int d_dst, s_dst;        // LDS destinations inside a stage
+  uint32_t s_voff;         // scale copies: this lane's row
+  int d_dst, s_dst;        // LDS destinations inside a stage's A / B and scale regions
 };
 
-// Copies of stage kb into the stage at `st`: 4 KiB of A codes, 4 KiB of B codes and 1 KiB of
-// scales per wave.
+// Copies of stage kb into the stage at `st`: 8 KiB of A codes, 8 KiB of B codes and 1 KiB each
+// of A and B scales per wave.
 __device__ __forceinline__ void copy_stage(uint8_t* __restrict__ st, const NvLoadPlan& lp, int kb) {
   const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
 #pragma unroll
@@ -66,7 +67,8 @@ __device__ __forceinline__ void copy_stage(uint8_t* __restrict__ st, const NvLoa
     buf2lds16(lp.a_rsrc, lp.voff[i], k * ROWB, as_lds(st + A_OFF + lp.d_dst + i * 1024));
     buf2lds16(lp.b_rsrc, lp.voff[i], k * ROWB, as_lds(st + B_OFF + lp.d_dst + i * 1024));
   }
-  buf2lds16(lp.s_rsrc, lp.s_voff, k * SROWB, as_lds(st + lp.s_dst));
+  buf2lds16(lp.sa_rsrc, lp.s_voff, k * SROWB, as_lds(st + SA_OFF + lp.s_dst));
+  buf2lds16(lp.sb_rsrc, lp.s_voff, k * SROWB, as_lds(st + SB_OFF + lp.s_dst));
 }
 
 // 8 f16 operand values from one dword of e2m1 codes (bytes 0..3, two codes each), times the
@@ -79,14 +81,25 @@ __device__ __forceinline__ h8 decode8(uint32_t d, h2 sc) {
   return (h8){c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 }
 
-// The two e4m3 scales of half h of a lane's scale dword (bytes 2h and 2h+1) as f16, each
-// broadcast to both halves of a pair: [0] for steps 0-1, [1] for steps 2-3.
-template <int H>
-__device__ __forceinline__ void half_scales(uint32_t sd, h2 (&out)[2]) {
-  const h2 p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sd, 1.0f, H != 0);
-  out[0] = (h2){p[0], p[0]};
-  out[1] = (h2){p[1], p[1]};
+// Two e2m1 codes (byte `sel` of d) to f16, exactly (scale input 1).
+__device__ __forceinline__ h2 cvt_fp4_pair(uint32_t d, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
+  }
 }
+
+// acc += b^T-fragment x a-fragment, in place. Written as an instruction with the accumulator
+// tied to its AGPRs: through the builtin the register allocator gives the result new AGPRs and
+// copies, which with all 256 AGPRs holding accumulators spills into VGPRs.
+__device__ __forceinline__ void mfma_acc(v4f& acc, const h8& b, const h8& a) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// An empty use that keeps a value in its registers up to this point.
+__device__ __forceinline__ void keep_live(const h8& x) { asm volatile("" ::"v"(x)); }
 
 template <int OUT>
 __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_blocks) {
@@ -99,7 +112,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
   if (!work_item(num_super, n_blocks, 8, s, nb)) return;
   const int n0 = nb * BN, N = p.N, KB = p.K / KSTAGE;
   const size_t rowb = (size_t)p.K / 2, srow = (size_t)p.K / 16;   // bytes per row: codes, scales
-  const int wm = wave >> 1, wn = wave & 1;                        // rows 64 wm, cols 128 wn
+  const int wm = wave >> 1, wn = wave & 1;                        // rows 128 wm, cols 128 wn
   const int r16 = lane & 15, q = lane >> 4;
   const int ncols = min(BN, N - n0);
 
@@ -143,20 +156,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
     NvLoadPlan lp;
     lp.a_rsrc = make_rsrc((const uint8_t*)p.A + (size_t)row0 * rowb, (uint64_t)rows * rowb);
     lp.b_rsrc = make_rsrc((const uint8_t*)p.B + ((size_t)e * N + n0) * rowb, (uint64_t)ncols * rowb);
-    if (wave < 4)
-      lp.s_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)row0 * srow, (uint64_t)rows * srow);
-    else
-      lp.s_rsrc = make_rsrc((const uint8_t*)p.b_scales + ((size_t)e * N + n0) * srow, (uint64_t)ncols * srow);
+    lp.sa_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)row0 * srow, (uint64_t)rows * srow);
+    lp.sb_rsrc = make_rsrc((const uint8_t*)p.b_scales + ((size_t)e * N + n0) * srow, (uint64_t)ncols * srow);
     {
       const int lrow = lane >> 3, slot = lane & 7;
-      // copy i of wave w covers rows 32 w + 8 i + lrow; swz8 of such a row is lrow ^ (i & 1)
+      // copy i of wave w covers rows 64 w + 8 i + lrow; swz8 of such a row is lrow ^ (i & 1)
 #pragma unroll
       for (int i = 0; i < D_INSTR; i++)
-        lp.voff[i] = (uint32_t)((wave * 32 + i * 8 + lrow) * rowb + ((slot ^ lrow ^ (i & 1)) * 16));
+        lp.voff[i] = (uint32_t)((wave * 64 + i * 8 + lrow) * rowb + ((slot ^ lrow ^ (i & 1)) * 16));
       lp.d_dst = wave * D_INSTR * 1024;
-      // scale copy of wave w: rows 64 (w % 4) + lane, 16 bytes each, stored row after row
-      lp.s_voff = (uint32_t)(((wave & 3) * 64 + lane) * srow);
-      lp.s_dst = (wave < 4 ? SA_OFF : SB_OFF) + (wave & 3) * 1024;
+      // scale copies of wave w: rows 64 w + lane of A and of B, 16 bytes each, row after row
+      lp.s_voff = (uint32_t)((wave * 64 + lane) * srow);
+      lp.s_dst = wave * 1024;
     }
 
     v4f acc[MI][NJ];
@@ -175,49 +186,116 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
       // barrier that closed stage b-1
       if (b + 1 < KB) copy_stage(smem + ((b + 1) & 1) * STAGE_BYTES, lp, b + 1);
 
-      uint32_t asd[MI], bsd[NJ];
+      // Scales of the stage: lane's dword of each A and B fragment row, decoded per half h into
+      // f16 pairs (the scale of steps 4h, 4h+1 in [0], of 4h+2, 4h+3 in [1]).
+      h2 as2[MI][2], bs2[NJ][2];
 #pragma unroll
-      for (int i = 0; i < MI; i++) asd[i] = *(const uint32_t*)(st + sa_off + i * 16 * SROWB);
+      for (int i = 0; i < MI; i++) {
+        const uint32_t sd = *(const uint32_t*)(st + sa_off + i * 16 * SROWB);
+        as2[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sd, 1.0f, false);
+        as2[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sd, 1.0f, true);
+      }
 #pragma unroll
-      for (int j = 0; j < NJ; j++) bsd[j] = *(const uint32_t*)(st + sb_off + j * 16 * SROWB);
+      for (int j = 0; j < NJ; j++) {
+        const uint32_t sd = *(const uint32_t*)(st + sb_off + j * 16 * SROWB);
+        bs2[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sd, 1.0f, false);
+        bs2[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sd, 1.0f, true);
+      }
+      // A codes: the lane's 16 bytes of each fragment row for steps 0-3 (half 0); those of half 1
+      // replace them at step 3, once the conversions for steps 1-3 are done
+      v4i apk[MI];
+#pragma unroll
+      for (int i = 0; i < MI; i++) apk[i] = lds_read16(st + da[0] + i * 16 * ROWB);
 
-      auto half = [&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        v4i apk[MI], bpk[NJ];
+      // 64 steps k = 8 u + j: step u of the stage's K (dword u of every lane's 32 bytes) against
+      // B fragment j. Each step issues its 8 MFMAs, then decodes the B operand of step k+1, reads
+      // the B dword of step k+2 and converts A fragment j for step u+1, so the VALU work of one
+      // step runs under the previous step's MFMAs.
+      auto b_dword = [&](int k) {
+        const int u = k >> 3, j = k & 7;
+        return *(const uint32_t*)(st + db[u >> 2] + j * 16 * ROWB + 4 * (u & 3));
+      };
+      auto scale_of = [](const h2 (&pr)[2], int u) {
+        const h2 p2 = pr[u >> 2];
+        return (u & 2) ? (h2){p2[1], p2[1]} : (h2){p2[0], p2[0]};
+      };
+      h8 avc[MI], avn[MI];
 #pragma unroll
-        for (int i = 0; i < MI; i++) apk[i] = lds_read16(st + da[h] + i * 16 * ROWB);
+      for (int i = 0; i < MI; i++) avc[i] = decode8((uint32_t)apk[i][0], scale_of(as2[i], 0));
+      h8 bv = decode8(b_dword(0), scale_of(bs2[0], 0));
+      uint32_t bw1 = b_dword(1);
 #pragma unroll
-        for (int j = 0; j < NJ; j++) bpk[j] = lds_read16(st + db[h] + j * 16 * ROWB);
-        h2 asc[MI][2], bsc[NJ][2];
+      for (int k = 0; k < 64; k++) {
+        const int u = k >> 3, j = k & 7;
+        const int u1 = (k + 1) >> 3, j1 = (k + 1) & 7;
+        uint32_t bw2 = 0;
+        if (k + 2 < 64) bw2 = b_dword(k + 2);
+        if (k == 24) {
 #pragma unroll
-        for (int i = 0; i < MI; i++) half_scales<h>(asd[i], asc[i]);
+          for (int i = 0; i < MI; i++) apk[i] = lds_read16(st + da[1] + i * 16 * ROWB);
+        }
+        const h2 sbn = scale_of(bs2[j1 & 7], u1 & 7);
+        const h2 san = scale_of(as2[j], (u + 1) & 7);
+        const uint32_t aw = (uint32_t)apk[j][(u + 1) & 3];
+        h2 bn[4], an[4];
+        // MFMA i, then two VALU ops: conversions of the B operand of step k+1 under MFMAs 0-1 and
+        // their scaling under MFMAs 2-3; the same for A fragment j of step u+1 under MFMAs 4-7.
+        // A product is scaled two MFMAs after its conversion, so no op waits on the one before.
 #pragma unroll
-        for (int j = 0; j < NJ; j++) half_scales<h>(bsd[j], bsc[j]);
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          h8 av[MI];
-#pragma unroll
-          for (int i = 0; i < MI; i++) av[i] = decode8((uint32_t)apk[i][t], asc[i][t >> 1]);
-#pragma unroll
-          for (int j = 0; j < NJ; j++) {
-            const h8 bv = decode8((uint32_t)bpk[j][t], bsc[j][t >> 1]);
-#pragma unroll
-            for (int i = 0; i < MI; i++)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, av[i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < MI; i++) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_acc(acc[i][j], bv, avc[i]);
+          const int p0 = 2 * (i & 1);
+          if (i < 4) {
+            if (k + 1 < 64) {
+              if (i < 2) {
+                bn[p0] = cvt_fp4_pair(bw1, p0);
+                bn[p0 + 1] = cvt_fp4_pair(bw1, p0 + 1);
+              } else {
+                bn[p0] = bn[p0] * sbn;
+                bn[p0 + 1] = bn[p0 + 1] * sbn;
+              }
+            }
+          } else if (u < 7) {
+            if (i < 6) {
+              an[p0] = cvt_fp4_pair(aw, p0);
+              an[p0 + 1] = cvt_fp4_pair(aw, p0 + 1);
+            } else {
+              an[p0] = an[p0] * san;
+              an[p0 + 1] = an[p0 + 1] * san;
+            }
           }
         }
-      };
-      half(std::integral_constant<int, 0>());
-      half(std::integral_constant<int, 1>());
+        __builtin_amdgcn_sched_barrier(0);
+        // the operands read by this step's MFMAs stay live until here, so the registers written
+        // above are others
+        keep_live(bv);
+        if (k + 1 < 64) bv = (h8){bn[0][0], bn[0][1], bn[1][0], bn[1][1], bn[2][0], bn[2][1], bn[3][0], bn[3][1]};
+        if (u < 7) avn[j] = (h8){an[0][0], an[0][1], an[1][0], an[1][1], an[2][0], an[2][1], an[3][0], an[3][1]};
+        if (j == NJ - 1) {
+#pragma unroll
+          for (int i = 0; i < MI; i++) {
+            keep_live(avc[i]);
+            avc[i] = avn[i];
+          }
+        }
+        bw1 = bw2;
+      }
       // this wave's copies of stage b+1 have landed and its reads of stage b are done; after the
       // barrier every wave's are
       wait_vmcnt<0>();
       barrier();
     }
 
-    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N fragment
+    // the last MFMAs' results are read by VALU below: give them the wait states the compiler
+    // cannot see through the instructions written by hand
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N
+    // fragment; one M fragment at a time, so that only its 32 accumulators sit in VGPRs
 #pragma unroll
     for (int i = 0; i < MI; i++) {
+      __builtin_amdgcn_sched_barrier(0);
       const int mloc = wm * WM + i * 16 + r16;
       if (mloc >= rows) continue;
       const size_t crow = (size_t)(row0 + mloc) * N;
