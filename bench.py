@@ -20,6 +20,11 @@ With --workload nvfp4_8192 a step is one dense nvfp4 GEMM of 8192^3 (e2m1 elemen
 scale per 16 K, fp16 out); the products run on the f16 matrix instruction, so its roofline is
 against the f16 peak.
 
+With --workload dense_4096 (one group 4096^3, every 64th row of A and B x100) or moe8_n2048_k4096
+(8 experts, 4096 tokens at top-2, Dirichlet(0.5), N=2048, K=4096) a step is the tile map (grouped
+only) and one blockwise-FP8 GEMM launch, bf16 out; its roofline is that launch against the FP8
+peak.
+
 With --workload permute_moe32 a step is the step before the GEMM on the same routing: per-expert
 counts of the top-8 picks, the tile map, and the permutation of the 16384 bf16 token rows
 (K = 7168) into the padded expert-sorted A with e4m3 1x128 quantisation. It is HBM-bound: the
@@ -74,10 +79,13 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="moe32",
                     choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
-                             "nvfp4_8192", "permute_moe32", "decode_moe32"])
+                             "nvfp4_8192", "permute_moe32", "decode_moe32", "dense_4096",
+                             "moe8_n2048_k4096"])
     ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
                     help="K of the mx8192_* and nvfp4_8192 workloads (M = N = 8192; the pages' "
                          "K sweep runs 512 .. 8192)")
+    ap.add_argument("--sched-small-m", action="store_true",
+                    help="dense_4096 / moe8_n2048_k4096: request the one-M-tile-per-item schedule")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB "
                          "MiB each (a kernel of known traffic for scaling HBM counters) and exit")
@@ -114,7 +122,7 @@ def cpu_baseline(problems, n_experts=16, rows_per_expert=128):
     }
 
 
-def cpu_baseline_mx(p, rows=1024):
+def cpu_baseline_mx(p, rows=8192):
     """Time the oracle on the first ``rows`` rows of A of the MX GEMM (all N, all K)."""
     from threadpoolctl import threadpool_info
 
@@ -398,6 +406,95 @@ def cpu_baseline_decode(p, counts, ei, to, nbytes, n_experts=4):
     }
 
 
+def bench_blockwise(args, torch, bsg, make_problem):
+    """A step is the tile map (grouped workloads) plus one blockwise-FP8 GEMM launch, bf16 out."""
+    from oracle import gemm as og
+    from threadpoolctl import threadpool_info
+    from workloads.generate import padded_starts
+
+    p = make_problem(args.workload, device="cuda", seed=args.seed)
+    dev = p.qa.device
+    stream = torch.cuda.current_stream()
+    C = torch.empty(p.M, p.N, dtype=torch.bfloat16, device=dev)
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16", small_m=args.sched_small_m)
+    grouped = p.counts is not None
+    T = p.M // 128
+    if grouped:
+        counts = torch.tensor(p.counts, dtype=torch.int32, device=dev)
+        eo = torch.empty(p.E + 1, dtype=torch.int32, device=dev)
+        to = torch.empty(T + 1, dtype=torch.int32, device=dev)
+        ei = torch.empty(T, dtype=torch.int32, device=dev)
+    gemm_ev = []
+
+    def step(record):
+        if grouped:
+            bsg.bsgemm_build_tiles(counts, T, True, eo, to, ei, stream)
+        a = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            a.record(stream)
+        bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei if grouped else None,
+                           to if grouped else None, C, p.M, p.N, p.K, fmt, num_tiles=T,
+                           num_experts=p.E, stream=stream)
+        if record:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            gemm_ev.append((a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in gemm_ev]))
+    flops = p.useful_flops
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    desc = {"dense_4096": "one group 4096^3, every 64th row of A and B x100",
+            "moe8_n2048_k4096": "8 experts, 4096 tokens x top-2, Dirichlet(0.5), N=2048, K=4096"}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2), "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {desc[args.workload]}, blockwise e4m3 "
+                               f"1x128/128x128 fp32 scales, bf16 out", "real_rows": p.real_rows,
+                   "padded_rows": p.M, "N": p.N, "K": p.K, "experts": p.E, "seed": args.seed},
+        "kernels_ms": {"gemm": round(kernel_ms, 4)},
+        "roofline": {"kernel": "bw_fp8_small_m_kernel" if args.sched_small_m else "bw_fp8_grouped_kernel",
+                     "bound": "mfma",
+                     "achieved": round(kernel_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on about 10 s of work: dense, all 4096 rows; grouped, up to 512 real rows of
+        # each expert
+        if grouped:
+            starts = padded_starts(p.counts)
+            parts = [(e, int(starts[e]), min(512, int(p.counts[e]))) for e in range(p.E)
+                     if p.counts[e] > 0]
+        else:
+            parts = [(0, 0, p.M)]
+        work = [(p.qa[s0:s0 + r].cpu().numpy(), p.a_scales[s0:s0 + r].cpu().numpy(),
+                 p.qb[e].cpu().numpy(), p.b_scales[e].cpu().numpy()) for e, s0, r in parts]
+        t1 = time.perf_counter()
+        for qa, sa, qb, sb in work:
+            og.blockwise_grouped(qa, sa, qb, sb)
+        dt = time.perf_counter() - t1
+        rows = sum(r for _, _, r in parts)
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        out["cpu_baseline"] = {
+            "value": 2.0 * rows * p.N * p.K / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} real rows x N={p.N} x K={p.K} of {args.workload}, fp64 oracle K "
+                      f"block by K block; {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -432,6 +529,9 @@ def main():
         return
     if args.workload == "decode_moe32":
         bench_decode(args, torch, bsg)
+        return
+    if args.workload in ("dense_4096", "moe8_n2048_k4096"):
+        bench_blockwise(args, torch, bsg, make_problem)
         return
     if args.workload != "moe32":
         bench_mx(args, torch, bsg, make_problem)
