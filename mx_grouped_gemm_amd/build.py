@@ -60,7 +60,9 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        extra = [] if src in AGPR_ACC_SOURCES else VGPR_FORM
+        # a loop the source requires unrolled (#pragma clang loop unroll(full)) that the compiler
+        # cannot unroll is a build error
+        extra = ["-Werror=pass-failed"] if src in AGPR_ACC_SOURCES else VGPR_FORM
         cmds.append([hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for out in ex.map(_run, cmds):

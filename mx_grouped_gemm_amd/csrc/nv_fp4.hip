@@ -58,17 +58,23 @@ struct NvLoadPlan {
   int d_dst, s_dst;        // LDS destinations inside a stage's A / B and scale regions
 };
 
-// Copies of stage kb into the stage at `st`: 8 KiB of A codes, 8 KiB of B codes and 1 KiB each
-// of A and B scales per wave.
-__device__ __forceinline__ void copy_stage(uint8_t* __restrict__ st, const NvLoadPlan& lp, int kb) {
+// Copy c (of COPIES per wave) of stage kb into the stage at `st`: 8 KiB of A codes, 8 KiB of B
+// codes and 1 KiB each of A and B scales per wave.
+constexpr int COPIES = 2 * D_INSTR + 2;
+__device__ __forceinline__ void copy_one(uint8_t* __restrict__ st, const NvLoadPlan& lp, int kb, int c) {
   const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+  if (c < D_INSTR)
+    buf2lds16(lp.a_rsrc, lp.voff[c], k * ROWB, as_lds(st + A_OFF + lp.d_dst + c * 1024));
+  else if (c < 2 * D_INSTR)
+    buf2lds16(lp.b_rsrc, lp.voff[c - D_INSTR], k * ROWB, as_lds(st + B_OFF + lp.d_dst + (c - D_INSTR) * 1024));
+  else if (c == 2 * D_INSTR)
+    buf2lds16(lp.sa_rsrc, lp.s_voff, k * SROWB, as_lds(st + SA_OFF + lp.s_dst));
+  else
+    buf2lds16(lp.sb_rsrc, lp.s_voff, k * SROWB, as_lds(st + SB_OFF + lp.s_dst));
+}
+__device__ __forceinline__ void copy_stage(uint8_t* __restrict__ st, const NvLoadPlan& lp, int kb) {
 #pragma unroll
-  for (int i = 0; i < D_INSTR; i++) {
-    buf2lds16(lp.a_rsrc, lp.voff[i], k * ROWB, as_lds(st + A_OFF + lp.d_dst + i * 1024));
-    buf2lds16(lp.b_rsrc, lp.voff[i], k * ROWB, as_lds(st + B_OFF + lp.d_dst + i * 1024));
-  }
-  buf2lds16(lp.sa_rsrc, lp.s_voff, k * SROWB, as_lds(st + SA_OFF + lp.s_dst));
-  buf2lds16(lp.sb_rsrc, lp.s_voff, k * SROWB, as_lds(st + SB_OFF + lp.s_dst));
+  for (int c = 0; c < COPIES; c++) copy_one(st, lp, kb, c);
 }
 
 // 8 f16 operand values from one dword of e2m1 codes (bytes 0..3, two codes each), times the
@@ -94,8 +100,22 @@ __device__ __forceinline__ h2 cvt_fp4_pair(uint32_t d, int sel) {
 // acc += b^T-fragment x a-fragment, in place. Written as an instruction with the accumulator
 // tied to its AGPRs: through the builtin the register allocator gives the result new AGPRs and
 // copies, which with all 256 AGPRs holding accumulators spills into VGPRs.
+// The compiler does not see this instruction's hazards, so the code around it keeps them:
+//  * a VALU write of a source VGPR needs 2 wait states before the MFMA reads it. The operands of
+//    a step are built during the previous step, but the compiler may place their last writes (or
+//    register moves) right at the step boundary, so the first MFMA of every step (WAIT = true)
+//    starts with s_nop 4 (5 wait states, a margin over the 2 required); the others follow it by
+//    at least one instruction more than it.
+//  * the sources stay live until the end of the step (keep_live), so no VALU overwrites them
+//    while the step's MFMAs read them; the accumulators are never VALU-written in the K loop.
+//  * VALU reads of the results wait explicitly before the epilogue, and the accumulators are
+//    zeroed well before the first MFMA.
+template <bool WAIT>
 __device__ __forceinline__ void mfma_acc(v4f& acc, const h8& b, const h8& a) {
-  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+  if constexpr (WAIT)
+    asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
 // An empty use that keeps a value in its registers up to this point.
@@ -174,7 +194,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
 #pragma unroll
     for (int i = 0; i < MI; i++)
 #pragma unroll
-      for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; j++) {
+        acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+a"(acc[i][j]));   // written to its AGPRs here, before the wait below
+      }
+    // wait states between those VALU writes and the first MFMA that reads them
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
     copy_stage(smem, lp, 0);
     wait_vmcnt<0>();
@@ -183,8 +208,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
     for (int b = 0; b < KB; b++) {
       const uint8_t* st = smem + (b & 1) * STAGE_BYTES;
       // stage b+1 goes into the other buffer, whose last reads (stage b-1) ended before the
-      // barrier that closed stage b-1
-      if (b + 1 < KB) copy_stage(smem + ((b + 1) & 1) * STAGE_BYTES, lp, b + 1);
+      // barrier that closed stage b-1; its copies are spread one per step over steps 1..18, so
+      // that no run of copies holds up this wave's MFMA issue (in the last stage they repeat
+      // stage KB-1 into a buffer that is not read again: a branch around them would stop the
+      // step loop from being unrolled, which this kernel requires)
+      uint8_t* const nxt = smem + ((b + 1) & 1) * STAGE_BYTES;
 
       // Scales of the stage: lane's dword of each A and B fragment row, decoded per half h into
       // f16 pairs (the scale of steps 4h, 4h+1 in [0], of 4h+2, 4h+3 in [1]).
@@ -224,7 +252,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
       for (int i = 0; i < MI; i++) avc[i] = decode8((uint32_t)apk[i][0], scale_of(as2[i], 0));
       h8 bv = decode8(b_dword(0), scale_of(bs2[0], 0));
       uint32_t bw1 = b_dword(1);
-#pragma unroll
+      // Fully unrolled (the build fails otherwise): the hand-written MFMAs need every
+      // accumulator in fixed AGPRs; indexed at run time they would move through VGPRs next to
+      // instructions whose wait states the compiler does not know.
+#pragma clang loop unroll(full)
       for (int k = 0; k < 64; k++) {
         const int u = k >> 3, j = k & 7;
         const int u1 = (k + 1) >> 3, j1 = (k + 1) & 7;
@@ -244,7 +275,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
 #pragma unroll
         for (int i = 0; i < MI; i++) {
           __builtin_amdgcn_sched_barrier(0);
-          mfma_acc(acc[i][j], bv, avc[i]);
+          if (i == 0)
+            mfma_acc<true>(acc[i][j], bv, avc[i]);
+          else
+            mfma_acc<false>(acc[i][j], bv, avc[i]);
           const int p0 = 2 * (i & 1);
           if (i < 4) {
             if (k + 1 < 64) {
@@ -266,6 +300,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void nv_fp4_kernel(GemmArgs p, int n_b
             }
           }
         }
+        if (k >= 1 && k <= COPIES) copy_one(nxt, lp, min(b + 1, KB - 1), k - 1);
         __builtin_amdgcn_sched_barrier(0);
         // the operands read by this step's MFMAs stay live until here, so the registers written
         // above are others
