@@ -126,3 +126,31 @@ def test_nvfp4_8192_sampled():
     check(p, "f16", C, rows=sample_rows(p, per_tile=2), label="nvfp4_8192")
     del C, p
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K", [512, 1024, 2048, 4096])
+def test_nv_k_sweep(K):
+    """The K values of the pages' benchmark sweep (M = N = 1024 here so the oracle is quick)."""
+    p = nv_problem(1024, 1024, K, device="cuda", seed=K + 7)
+    C, _, _ = run_problem(p, "f16")
+    check(p, "f16", C, rows=sample_rows(p, per_tile=4), label=f"nvfp4 sweep K={K}")
+
+
+def test_nv_skipped_and_out_of_range_tiles():
+    """Tiles with id -1 or an id >= num_experts are skipped: their rows keep the poison."""
+    p = nv_problem(0, 256, 512, device="cuda", seed=48, counts=[128, 128])
+    ei = torch.tensor([1, -1, 0, 9], dtype=torch.int32, device="cuda")
+    to = torch.tensor([0, 128, 256, 384, 512], dtype=torch.int32, device="cuda")
+    M = 512
+    qa = torch.cat([p.qa, torch.zeros(M - p.M, p.K // 2, dtype=torch.uint8, device="cuda")])
+    sa = torch.cat([p.a_scales, torch.full((M - p.M, p.K // 16), 0x38, dtype=torch.uint8, device="cuda")])
+    C = _run(qa, sa, p.qb, p.b_scales, M, p.N, p.K, "f32", ei, to, E=2)
+    assert torch.all(torch.isnan(C[128:256])) and torch.all(torch.isnan(C[384:]))
+    args = [t.cpu().numpy() for t in (qa, sa, p.qb, p.b_scales)]
+    ei_r, to_r = np.array([1, -1, 0, -1]), to.cpu().numpy()
+    ref = og.nv_gemm(*args, ei_r, to_r)
+    den = og.nv_gemm(*args, ei_r, to_r, absolute=True)
+    live = np.r_[0:128, 256:384]
+    err = og.relative_error(C.cpu().numpy()[live], ref[live], den[live])
+    say(f"[nv-skip] max_rel_err={err:.3e}")
+    assert err <= 1e-3
