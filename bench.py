@@ -64,10 +64,29 @@ GATE_UP_TRAFFIC = ("562d521271a595ad", 12.52e9)
 KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
 
 
+# The same for the 8192^3 launches (K = 8192) of other kernels: workload -> (source file, sha256
+# prefix of that source, HBM bytes per launch).
+SINGLE_TRAFFIC = {
+    "nvfp4_8192": ("nv_fp4.hip", "b258747ffe9334c2", 0.590e9),
+    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "20af0c6fd2092647", 0.991e9),
+}
+
+
+def _source_matches(path, prefix):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest().startswith(prefix)
+
+
 def measured_traffic():
-    with open(KERNEL_SOURCE, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return GATE_UP_TRAFFIC[1] if digest.startswith(GATE_UP_TRAFFIC[0]) else None
+    return GATE_UP_TRAFFIC[1] if _source_matches(KERNEL_SOURCE, GATE_UP_TRAFFIC[0]) else None
+
+
+def measured_traffic_single(workload, K):
+    if workload not in SINGLE_TRAFFIC or K != 8192:
+        return None
+    src, prefix, nbytes = SINGLE_TRAFFIC[workload]
+    path = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", src)
+    return nbytes if _source_matches(path, prefix) else None
 
 
 def parse():
@@ -214,7 +233,8 @@ def bench_mx(args, torch, bsg, make_problem):
             "kernel": "nv_fp4_kernel (f16 MFMA)" if nv else f"mx_kernel<{p.fmt_a}, {p.fmt_b}>",
             "bound": "mfma",
             "achieved": round(kernel_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(kernel_tflops / peak, 4), "traffic": None,
+            "frac": round(kernel_tflops / peak, 4),
+            "traffic": measured_traffic_single(args.workload, p.K),
         },
     }
     if not args.no_cpu_baseline:
