@@ -67,7 +67,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_groupe
 # The same for the 8192^3 launches (K = 8192) of other kernels: workload -> (source file, sha256
 # prefix of that source, HBM bytes per launch).
 SINGLE_TRAFFIC = {
-    "nvfp4_8192": ("nv_fp4.hip", "b258747ffe9334c2", 0.590e9),
+    "nvfp4_8192": ("nv_fp4.hip", "0c838a70d41842ac", 0.590e9),
     "mx8192_e4m3_e4m3": ("mx_scaled.hip", "20af0c6fd2092647", 0.991e9),
 }
 

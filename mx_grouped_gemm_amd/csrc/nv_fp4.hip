@@ -16,8 +16,9 @@
 // accumulators in AGPRs. The conversions are VALU work in proportion to the wave tile's rows plus
 // columns, and they, not the matrix unit, bound this kernel: 128 x 128 needs a third fewer per
 // product than 64 x 128 (8 waves, two per SIMD measured 0.50 of the f16 peak). A 2-stage LDS ring of
-// 256-K stages filled by buffer -> LDS copies (stage b+1 is copied while stage b is computed),
-// one barrier per stage. A stage row is 128 bytes of codes and 16 bytes of scales.
+// 256-K stages filled by buffer -> LDS copies (stage b+1 is copied while stage b is computed, one
+// copy per step), one barrier per stage. A stage row is 128 bytes of codes and 16 bytes of scales.
+// The MFMA is written by hand (see mfma_acc), so this file keeps that instruction's hazards itself.
 //
 // K order inside a stage. The sum over K does not depend on which K elements a lane feeds to
 // which instruction, as long as both operands use the same assignment. Lane (r16, q) of a
@@ -101,7 +102,8 @@ __device__ __forceinline__ h2 cvt_fp4_pair(uint32_t d, int sel) {
 // tied to its AGPRs: through the builtin the register allocator gives the result new AGPRs and
 // copies, which with all 256 AGPRs holding accumulators spills into VGPRs.
 // The compiler does not see this instruction's hazards, so the code around it keeps them:
-//  * a VALU write of a source VGPR needs 2 wait states before the MFMA reads it. The operands of
+//  * a VALU write of a source VGPR needs 2 wait states before the MFMA reads it (the compiler's
+//    own MFMA hazard rules ask for that many after a VALU write of a source). The operands of
 //    a step are built during the previous step, but the compiler may place their last writes (or
 //    register moves) right at the step boundary, so the first MFMA of every step (WAIT = true)
 //    starts with s_nop 4 (5 wait states, a margin over the 2 required); the others follow it by
