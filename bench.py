@@ -187,28 +187,25 @@ def bench_mx(args, torch, bsg, make_problem):
     C = torch.empty(p.M, p.N, dtype=torch.float16, device="cuda")
     fmt = bsg.make_fmt(p.fmt_a, p.fmt_b, p.scale_kind, "f16")
     stream = torch.cuda.current_stream()
-    launches = []
 
-    def step(record):
-        a = torch.cuda.Event(enable_timing=True) if record else None
-        if record:
-            a.record(stream)
+    def step():
         bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C, p.M, p.N, p.K, fmt,
                            num_tiles=p.M // 128, num_experts=1, stream=stream)
-        if record:
-            b = torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            launches.append((a, b))
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
+    # a step is one launch: the timed launches run back to back between two events on the launch
+    # stream, so the per-launch time carries no event overhead
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record(stream)
     for _ in range(args.steps):
-        step(True)
+        step()
+    b.record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in launches]))
+    kernel_ms = a.elapsed_time(b) / args.steps
     flops = p.useful_flops
     if nv:
         # the products run on the f16 matrix instruction (the e4m3 scales are folded into f16
@@ -444,31 +441,35 @@ def bench_blockwise(args, torch, bsg, make_problem):
         eo = torch.empty(p.E + 1, dtype=torch.int32, device=dev)
         to = torch.empty(T + 1, dtype=torch.int32, device=dev)
         ei = torch.empty(T, dtype=torch.int32, device=dev)
-    gemm_ev = []
 
-    def step(record):
-        if grouped:
-            bsg.bsgemm_build_tiles(counts, T, True, eo, to, ei, stream)
-        a = torch.cuda.Event(enable_timing=True) if record else None
-        if record:
-            a.record(stream)
+    def gemm():
         bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei if grouped else None,
                            to if grouped else None, C, p.M, p.N, p.K, fmt, num_tiles=T,
                            num_experts=p.E, stream=stream)
-        if record:
-            b = torch.cuda.Event(enable_timing=True)
-            b.record(stream)
-            gemm_ev.append((a, b))
+
+    def step():
+        if grouped:
+            bsg.bsgemm_build_tiles(counts, T, True, eo, to, ei, stream)
+        gemm()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in gemm_ev]))
+    # The kernel's own duration: the same number of GEMM launches back to back between two
+    # events on the launch stream (a pair of events around each launch of a kernel this short
+    # adds about a tenth to it).
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        gemm()
+    b.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = a.elapsed_time(b) / args.steps
     flops = p.useful_flops
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
