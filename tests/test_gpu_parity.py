@@ -111,6 +111,16 @@ def test_dense_ragged_m_and_n_tail():
     check(p, "bf16", C, label="dense M=200 N=384")
 
 
+@pytest.mark.parametrize("M", [64, 65, 192, 320])
+def test_dense_short_passes(M):
+    """Passes shorter than 256 rows: the waves whose 64 rows lie past the pass skip their matrix
+    work (M = 64: three of four row groups idle; 65: one row in the second group; 192: a merged
+    pass with the last group idle; 320: a full pass, then a 64-row one)."""
+    p = blockwise_problem(None, 512, 640, device="cuda", seed=M, a_rows=M, E=1)
+    C, _, _ = run_problem(p, "f32")
+    check(p, "f32", C, label=f"dense short M={M}")
+
+
 def test_grouped_padded_with_empty_experts():
     counts = [5, 0, 130, 17, 0, 300]
     p = blockwise_problem(counts, 256, 640, device="cuda", seed=4)
