@@ -103,6 +103,10 @@ def parse():
     ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
                     help="K of the mx8192_* and nvfp4_8192 workloads (M = N = 8192; the pages' "
                          "K sweep runs 512 .. 8192)")
+    ap.add_argument("--cold", action="store_true",
+                    help="single-launch workloads: before each timed launch write 512 MiB of "
+                         "scratch (untimed) so no operand is left in the caches; report the "
+                         "median and minimum launch time")
     ap.add_argument("--sched-small-m", action="store_true",
                     help="dense_4096 / moe8_n2048_k4096: request the one-M-tile-per-item schedule")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -168,6 +172,23 @@ def cpu_baseline_mx(p, rows=8192):
 KIND_NAME = {"mx": "MX", "nv": "nvfp4"}
 
 
+def time_cold(torch, stream, launch, steps):
+    """Per-launch times (ms) with a 512 MiB scratch write before each launch, outside the timed
+    events, so the operands come from HBM rather than from the 256 MB last-level cache."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    return times
+
+
 def bench_mx(args, torch, bsg, make_problem):
     """A step is one dense MX (or nvfp4) GEMM launch on a resident 8192 x 8192 x K problem."""
     nv = args.workload == "nvfp4_8192"
@@ -206,6 +227,7 @@ def bench_mx(args, torch, bsg, make_problem):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     kernel_ms = a.elapsed_time(b) / args.steps
+    cold = time_cold(torch, stream, step, args.steps) if args.cold else None
     flops = p.useful_flops
     if nv:
         # the products run on the f16 matrix instruction (the e4m3 scales are folded into f16
@@ -226,6 +248,9 @@ def bench_mx(args, torch, bsg, make_problem):
         "config": {"workload": f"{args.workload}: dense {KIND_NAME[p.scale_kind]} GEMM M=N=8192, "
                                f"K={p.K}, {scales} K, fp16 out", "K": p.K, "seed": args.seed},
         "kernels_ms": {"nvfp4" if nv else "mx": round(kernel_ms, 4)},
+        **({"cold_ms": {"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4),
+                        "tflops_at_median": round(flops / (np.median(cold) * 1e-3) / 1e12, 1)}}
+           if cold else {}),
         "roofline": {
             "kernel": "nv_fp4_kernel (f16 MFMA)" if nv else f"mx_kernel<{p.fmt_a}, {p.fmt_b}>",
             "bound": "mfma",
@@ -470,6 +495,7 @@ def bench_blockwise(args, torch, bsg, make_problem):
     b.record(stream)
     torch.cuda.synchronize()
     kernel_ms = a.elapsed_time(b) / args.steps
+    cold = time_cold(torch, stream, gemm, args.steps) if args.cold else None
     flops = p.useful_flops
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -485,6 +511,9 @@ def bench_blockwise(args, torch, bsg, make_problem):
                                f"1x128/128x128 fp32 scales, bf16 out", "real_rows": p.real_rows,
                    "padded_rows": p.M, "N": p.N, "K": p.K, "experts": p.E, "seed": args.seed},
         "kernels_ms": {"gemm": round(kernel_ms, 4)},
+        **({"cold_ms": {"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4),
+                        "tflops_at_median": round(flops / (np.median(cold) * 1e-3) / 1e12, 1)}}
+           if cold else {}),
         "roofline": {"kernel": "bw_fp8_small_m_kernel" if args.sched_small_m else "bw_fp8_grouped_kernel",
                      "bound": "mfma",
                      "achieved": round(kernel_tflops, 1), "peak": PEAK_FP8_TFLOPS,
