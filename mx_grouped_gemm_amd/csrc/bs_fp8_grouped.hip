@@ -70,7 +70,8 @@ constexpr int AS_INSTR = AS_BYTES / 256 / NWAVES;            // 4 (4-byte copies
 
 struct LoadPlan {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, bs_rsrc, as_rsrc;
-  uint32_t voff[A_INSTR];  // data copies: per-lane offset of instruction i (same for A and B)
+  uint32_t voff[A_INSTR];    // A copies: per-lane offset of instruction i
+  uint32_t voff_b[B_INSTR];  // B copies: the same with B's rows permuted (see b_col)
   uint32_t as_vrow;      // A scale chunk: lane part of the row offset
   uint32_t as_row8;      // A scale chunk: bytes of 8 rows of a_scales
   int a_dst, b_dst;
@@ -83,7 +84,7 @@ __device__ __forceinline__ void copy_a(uint8_t* __restrict__ da, const LoadPlan&
             as_lds(da + lp.a_dst + i * 1024));
 }
 __device__ __forceinline__ void copy_b(uint8_t* __restrict__ db, const LoadPlan& lp, int kb, int i) {
-  buf2lds16(lp.b_rsrc, lp.voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
+  buf2lds16(lp.b_rsrc, lp.voff_b[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
             as_lds(db + lp.b_dst + i * 1024));
 }
 __device__ __forceinline__ void copy_bs(uint8_t* __restrict__ dbs, const LoadPlan& lp, int kb, int wave) {
@@ -107,9 +108,22 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* p, const int (&base)[2])
   return cat(lds_read16(p + base[0]), lds_read16(p + base[1]));
 }
 
+// The partial of one fragment: the unscaled fp8 MFMA (both format fields e4m3). The builtin is
+// the scaled one; with both scale operands 0 the compiler emits v_mfma_f32_16x16x128_f8f6f4,
+// which applies no scale and saves the scaled form's extra instruction word.
 __device__ __forceinline__ v4f mma(const v8i& b, const v8i& a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                          127, 0, 127);
+                                                          0, 0, 0);
+}
+
+// Column (within its 128-column block) held by LDS row l of the B half. Fragment j of a wave
+// reads LDS rows 16 j .. 16 j + 15, and its MFMA gives lane (r16, q) the outputs of LDS rows
+// 16 j + 4 q .. 16 j + 4 q + 3. Mapping row 16 j + 4 q + i to column 32 (j / 2) + 8 q + 4 (j % 2) + i
+// gives the lane 8 consecutive columns in fragments 2 jj and 2 jj + 1: one 16-byte store of a
+// bf16 / fp16 result, and the 4 lanes of a row cover 64 consecutive bytes.
+__device__ __forceinline__ int b_col(int l) {
+  const int j = l >> 4, q = (l >> 2) & 3, i = l & 3;
+  return ((j >> 1) << 5) | (q << 3) | ((j & 1) << 2) | i;
 }
 
 template <int OUT>
@@ -183,8 +197,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       // Instruction i of wave w covers rows 32 w + 8 i + lrow (swz8 of that row is lrow ^ (i & 1)).
       // The whole row offset sits in the per-lane offset, which the resource bounds check.
 #pragma unroll
-      for (int i = 0; i < A_INSTR; i++)
-        lp.voff[i] = (uint32_t)((wave * 32 + i * 8 + lrow) * K + ((slot ^ lrow ^ (i & 1)) * 16));
+      for (int i = 0; i < A_INSTR; i++) {
+        const int l = wave * 32 + i * 8 + lrow;  // LDS row
+        const uint32_t chunk = (uint32_t)((slot ^ lrow ^ (i & 1)) * 16);
+        lp.voff[i] = (uint32_t)(l * K) + chunk;
+        lp.voff_b[i] = (uint32_t)(((l & 128) | b_col(l & 127)) * K) + chunk;
+      }
       lp.a_dst = wave * A_INSTR * 1024;
       lp.b_dst = wave * B_INSTR * 1024;
       // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow
@@ -347,17 +365,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       k_loop(std::false_type{});
     wait_vmcnt<0>();
 
-    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N
-    // fragment
+    // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
+    // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col)
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       const int mloc = wm * WM + i * 16 + r16;
       if (mloc >= rows) continue;
       const size_t crow = (size_t)(row0 + mloc) * N;
 #pragma unroll
-      for (int j = 0; j < NJ; j++) {
-        const int col = n0 + wn * WN + j * 16 + q * 4;
-        if (col < N) store4<OUT>(p.C, crow + col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int jj = 0; jj < NJ / 2; jj++) {
+        const int col = n0 + wn * WN + jj * 32 + q * 8;
+        if (col < N) store8<OUT>(p.C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
       }
     }
     if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass

@@ -9,7 +9,7 @@
 //
 //  * 8 waves, each owning 32 columns x the tile's rows as 8 x 2 fragments of 16 x 16; fragments
 //    past the last row are skipped (a wave-uniform test). The MFMA is the large-tile kernel's
-//    (v_mfma_scale_f32_16x16x128_f8f6f4, B rows as the first operand) with the same promotion
+//    (v_mfma_f32_16x16x128_f8f6f4, B rows as the first operand) with the same promotion
 //    order, so results are bitwise identical to it.
 //  * a 3-stage LDS ring (50 KiB per stage: 256 B rows and 128 A rows of 128 bytes, XOR-swizzled,
 //    plus scales) filled by buffer -> LDS copies two blocks ahead; every wave issues the same 7
@@ -40,7 +40,7 @@ constexpr int COPIES_PER_BLOCK = B_INSTR + A_INSTR + 1;
 
 __device__ __forceinline__ v4f mma(const v8i& b, const v8i& a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                          127, 0, 127);
+                                                          0, 0, 0);
 }
 
 struct Plan {

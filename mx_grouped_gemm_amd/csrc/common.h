@@ -98,6 +98,22 @@ __device__ __forceinline__ void store4(void* C, size_t off, float a, float b, fl
   }
 }
 
+// Store 8 consecutive fp32 values (lo, then hi) to C at element offset `off` (a multiple of 8):
+// one 16-byte store for bf16 / fp16, two for fp32.
+template <int OUT>
+__device__ __forceinline__ void store8(void* C, size_t off, const float __attribute__((ext_vector_type(4))) & lo,
+                                       const float __attribute__((ext_vector_type(4))) & hi) {
+  if constexpr (OUT == kOutF32) {
+    store4<OUT>(C, off, lo[0], lo[1], lo[2], lo[3]);
+    store4<OUT>(C, off + 4, hi[0], hi[1], hi[2], hi[3]);
+  } else {
+    uint32_t (*cv)(float) = OUT == kOutBF16 ? bf16_bits : f16_bits;
+    *(v4i*)((uint16_t*)C + off) =
+        (v4i){(int)(cv(lo[0]) | (cv(lo[1]) << 16)), (int)(cv(lo[2]) | (cv(lo[3]) << 16)),
+              (int)(cv(hi[0]) | (cv(hi[1]) << 16)), (int)(cv(hi[2]) | (cv(hi[3]) << 16))};
+  }
+}
+
 // Work order. Blocks are dispatched round-robin over the 8 XCDs (each with its own L2), so
 // block b runs on XCD b % 8. The grid is a multiple of 8 and block b takes logical item
 // (b % 8) * (grid / 8) + b / 8: the blocks resident on one XCD work on consecutive logical
