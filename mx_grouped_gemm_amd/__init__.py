@@ -13,6 +13,7 @@ import torch
 
 __all__ = [
     "BsgemmError", "ELEM", "SCALE", "OUT", "make_fmt", "bsgemm_build_tiles", "bsgemm_grouped",
+    "check_grouped_args", "check_permute_args",
     "bsgemm_status_string", "bsgemm_route_counts", "bsgemm_quantize_permute", "library_path",
     "load_library",
 ]
@@ -95,6 +96,67 @@ def _dev(t, name, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _byte_tensor(t, name, nbytes):
+    _need(t.element_size() == 1, f"{name} must hold one byte per element, got {t.dtype}")
+    _need(t.numel() >= nbytes, f"{name} holds {t.numel()} bytes, the call needs {nbytes}")
+
+
+def _f32_tensor(t, name, n):
+    _need(t.dtype == torch.float32, f"{name} must be float32, got {t.dtype}")
+    _need(t.numel() >= n, f"{name} holds {t.numel()} floats, the call needs {n}")
+
+
+def _i32_len(t, name, n):
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(t.numel() >= n, f"{name} holds {t.numel()} entries, the call needs {n}")
+
+
+_OUT_NAME = {v: k for k, v in OUT.items()}
+
+
+def check_grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, K, fmt,
+                       num_tiles, num_experts):
+    """Check that every tensor is large enough, and of the right type, for the sizes and ``fmt``
+    of a ``bsgemm_grouped`` call. The C ABI receives bare pointers and cannot check this: a
+    buffer that is too small would be read or written past its end on the GPU. Raises
+    ValueError. Sizes or formats the library itself rejects (negative sizes, N or K not a
+    multiple of 128, an unknown ``fmt``) are left to its status code."""
+    fa, fb, sk, out = fmt & 0xF, (fmt >> 4) & 0xF, (fmt >> 8) & 0xF, (fmt >> 12) & 0xF
+    if (M <= 0 or N <= 0 or K <= 0 or N % 128 or K % 128 or num_experts < 1 or num_tiles < 0
+            or fa not in (1, 2) or fb not in (1, 2) or sk not in (1, 2, 3) or out not in _OUT_NAME):
+        return
+    dense = expert_ids is None and tile_offsets is None
+    E = 1 if dense else num_experts
+    if not dense:
+        _need(expert_ids is not None and tile_offsets is not None,
+              "expert_ids and tile_offsets are both given or both None")
+        _i32_len(expert_ids, "expert_ids", num_tiles)
+        _i32_len(tile_offsets, "tile_offsets", num_tiles + 1)
+    row_a = K if fa == ELEM["e4m3"] else K // 2
+    row_b = K if fb == ELEM["e4m3"] else K // 2
+    _byte_tensor(A, "A", M * row_a)
+    _byte_tensor(B, "B", E * N * row_b)
+    if sk == SCALE["blockwise"]:
+        _f32_tensor(a_scales, "a_scales", M * (K // 128))
+        _f32_tensor(b_scales, "b_scales", E * (N // 128) * (K // 128))
+    else:
+        per = 32 if sk == SCALE["mx"] else 16
+        _byte_tensor(a_scales, "a_scales", M * (K // per))
+        _byte_tensor(b_scales, "b_scales", E * N * (K // per))
+    want = OUT_DTYPE[_OUT_NAME[out]]
+    _need(C.dtype == want, f"C must be {want} for this fmt, got {C.dtype}")
+    _need(C.numel() >= M * N, f"C holds {C.numel()} elements, the call needs {M * N}")
+
+
 def bsgemm_build_tiles(counts, num_tiles, padded=True, expert_offsets=None, tile_offsets=None,
                        expert_ids=None, stream=None):
     """Token-to-expert tile map from per-expert row counts (int32 device tensor).
@@ -112,6 +174,9 @@ def bsgemm_build_tiles(counts, num_tiles, padded=True, expert_offsets=None, tile
         expert_ids = torch.empty(max(num_tiles, 1), dtype=torch.int32, device=dev)
     for t, n in ((expert_offsets, "expert_offsets"), (tile_offsets, "tile_offsets"), (expert_ids, "expert_ids")):
         _dev(t, n, torch.int32)
+    _i32_len(expert_offsets, "expert_offsets", E + 1)
+    _i32_len(tile_offsets, "tile_offsets", num_tiles + 1)
+    _i32_len(expert_ids, "expert_ids", num_tiles)
     st = load_library().bsgemm_build_tiles(_ptr(counts), E, int(num_tiles), 1 if padded else 0,
                                            _ptr(expert_offsets), _ptr(tile_offsets),
                                            _ptr(expert_ids), _stream(stream))
@@ -135,6 +200,8 @@ def bsgemm_grouped(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, 
         num_tiles = expert_ids.numel() if expert_ids is not None else 0
     if num_experts is None:
         num_experts = B.shape[0] if B.dim() == 3 else 1
+    check_grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, int(M), int(N), int(K),
+                       int(fmt), int(num_tiles), int(num_experts))
     st = load_library().bsgemm_grouped(
         _ptr(A), _ptr(a_scales), _ptr(B), _ptr(b_scales), _ptr(expert_ids), _ptr(tile_offsets),
         int(num_tiles), _ptr(C), int(M), int(N), int(K), int(num_experts), int(fmt), _stream(stream))
@@ -149,11 +216,31 @@ def bsgemm_route_counts(topk_ids, num_experts, counts=None, stream=None):
     if counts is None:
         counts = torch.empty(num_experts, dtype=torch.int32, device=topk_ids.device)
     _dev(counts, "counts", torch.int32)
+    _i32_len(counts, "counts", num_experts)
     st = load_library().bsgemm_route_counts(_ptr(topk_ids), topk_ids.numel(), int(num_experts),
                                             _ptr(counts), _stream(stream))
     if st != 0:
         raise BsgemmError("bsgemm_route_counts", st)
     return counts
+
+
+def check_permute_args(x, topk_ids, expert_offsets, M, num_experts, dest, qa, a_scales):
+    """Size and type checks of a ``bsgemm_quantize_permute`` call that the C ABI cannot make
+    (see :func:`check_grouped_args`). Raises ValueError."""
+    _need(x.dim() == 2, f"x must be [tokens, K], got shape {tuple(x.shape)}")
+    tokens, K = x.shape
+    _need(topk_ids.dim() == 2 and topk_ids.shape[0] == tokens,
+          f"topk_ids must be [tokens={tokens}, top_k], got shape {tuple(topk_ids.shape)}")
+    top_k = topk_ids.shape[1]
+    if K <= 0 or K % 128 or M < 0 or num_experts < 1 or top_k < 1:
+        return
+    _i32_len(expert_offsets, "expert_offsets", num_experts + 1)
+    _i32_len(dest, "dest", tokens * top_k)
+    _need(tuple(qa.shape) == (M, K), f"qa must be [M={M}, K={K}], got shape {tuple(qa.shape)}")
+    _byte_tensor(qa, "qa", M * K)
+    _need(tuple(a_scales.shape) == (M, K // 128),
+          f"a_scales must be [M={M}, K/128={K // 128}], got shape {tuple(a_scales.shape)}")
+    _f32_tensor(a_scales, "a_scales", M * (K // 128))
 
 
 def bsgemm_quantize_permute(x, topk_ids, expert_offsets, M, num_experts, dest=None, qa=None,
@@ -177,6 +264,7 @@ def bsgemm_quantize_permute(x, topk_ids, expert_offsets, M, num_experts, dest=No
         a_scales = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
     for t, n in ((dest, "dest"), (qa, "qa"), (a_scales, "a_scales")):
         _dev(t, n)
+    check_permute_args(x, topk_ids, expert_offsets, M, num_experts, dest, qa, a_scales)
     x_dtype = OUT["f32"] if x.dtype == torch.float32 else OUT["bf16"]
     st = load_library().bsgemm_quantize_permute(
         _ptr(x), x_dtype, _ptr(topk_ids), int(tokens), int(top_k), int(K), int(num_experts),
