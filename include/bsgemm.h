@@ -53,9 +53,12 @@ typedef enum {
 #define BSG_FMT(a_elem, b_elem, scale, out) \
   ((uint32_t)(a_elem) | ((uint32_t)(b_elem) << 4) | ((uint32_t)(scale) << 8) | ((uint32_t)(out) << 12))
 /* Schedule hint (OR into fmt; blockwise only): M-tiles hold few rows (decode-sized expert
- * groups). Each work item is then one M-tile x 256 columns with the tile's rows taken 32 at a
- * time, instead of a 256 x 256 block tile. Same results, bit for bit (same instruction, operand
- * roles and promotion order); faster when most tiles hold well under 128 rows. */
+ * groups). Each work item is then one M-tile x 256 columns, and the matrix work stops at the
+ * tile's last row of 16-row fragments, instead of a 256 x 256 block tile. Same results, bit for
+ * bit (same instruction, operand roles and promotion order). Only the packed tile layout
+ * (bsgemm_build_tiles with padded == 0) has tiles of fewer than 128 rows: with the padded layout
+ * every tile spans 128 rows (padding included), so no fragment is skipped and the hint only
+ * changes the work item's shape. */
 #define BSG_SCHED_SMALL_M (1u << 16)
 
 /*
@@ -127,6 +130,15 @@ int bsgemm_build_tiles(const int32_t* counts, int32_t num_experts, int32_t num_t
  *   nvfp4 with A = B = e2m1 and K a multiple of 256 (else BSG_ERR_SHAPE), any output type.
  * Errors: BSG_ERR_NULL, BSG_ERR_SHAPE, BSG_ERR_ALIGN, BSG_ERR_FMT, BSG_ERR_DEVICE,
  *   BSG_ERR_LAUNCH.
+ */
+/*
+ * Arguments beyond the problem statement's list. The operation is named with the arguments
+ * (A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, K, fmt, stream). Two more are
+ * taken here: num_tiles, the length of expert_ids (a ragged, unpadded layout has a tile count
+ * that M does not determine, and the kernels never read past it), and num_experts, the leading
+ * dimension of B and b_scales ("promote_accumulators", Args: b_scales is shaped
+ * [num_experts, N // BN, K // BK]), so that an out-of-range expert id is skipped instead of
+ * addressing past B. Neither changes the result for a valid tile map.
  */
 int bsgemm_grouped(const void* A, const void* a_scales, const void* B, const void* b_scales,
                    const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles,
