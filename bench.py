@@ -115,33 +115,37 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(problems, n_experts=16, rows_per_expert=128):
-    """Time the oracle on a bounded sample: ``rows_per_expert`` real rows of each of the first
-    ``n_experts`` non-empty experts of the gate_up GEMM. Returns the JSON object."""
+def cpu_baseline(problems, n_experts=1):
+    """Time the oracle on a bounded sample of the step: every real row of the first ``n_experts``
+    non-empty experts, for both GEMMs (gate_up and down). The oracle is the product by its
+    definition (``blockwise_grouped_dequant``: decode and scale into fp64, then one BLAS product
+    per expert). Returns the JSON object."""
     from threadpoolctl import threadpool_info
 
     from oracle import gemm as og
     from workloads.generate import padded_starts
 
-    p = problems["gate_up"]
-    starts = padded_starts(p.counts)
-    experts = [e for e in range(p.E) if p.counts[e] > 0][:n_experts]
-    work, flops = [], 0.0
-    for e in experts:
-        r = min(rows_per_expert, int(p.counts[e]))
-        s = int(starts[e])
-        work.append((p.qa[s:s + r].cpu().numpy(), p.a_scales[s:s + r].cpu().numpy(),
-                     p.qb[e].cpu().numpy(), p.b_scales[e].cpu().numpy()))
-        flops += 2.0 * r * p.N * p.K
+    work, flops, rows = [], 0.0, 0
+    for name in ("gate_up", "down"):
+        p = problems[name]
+        starts = padded_starts(p.counts)
+        for e in [e for e in range(p.E) if p.counts[e] > 0][:n_experts]:
+            r, s0 = int(p.counts[e]), int(starts[e])
+            work.append((p.qa[s0:s0 + r].cpu().numpy(), p.a_scales[s0:s0 + r].cpu().numpy(),
+                         p.qb[e].cpu().numpy(), p.b_scales[e].cpu().numpy()))
+            flops += 2.0 * r * p.N * p.K
+            rows += r
     t0 = time.perf_counter()
     for qa, sa, qb, sb in work:
-        og.blockwise_grouped(qa, sa, qb, sb)
+        og.blockwise_grouped_dequant(qa, sa, qb, sb)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"gate_up GEMM, {rows_per_expert} real rows of each of {len(experts)} experts "
-                  f"(N={p.N}, K={p.K}), fp64 oracle K block by K block; {dt:.1f} s",
+        "sample": f"gate_up (N={problems['gate_up'].N}, K={problems['gate_up'].K}) and down "
+                  f"(N={problems['down'].N}, K={problems['down'].K}): every real row of the first "
+                  f"{n_experts} non-empty experts of each ({rows} rows in all); fp64 oracle by its "
+                  f"definition (decode and scale, then one BLAS product per expert); {dt:.1f} s",
     }
 
 

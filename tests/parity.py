@@ -87,11 +87,22 @@ def check(prob, out, C_gpu, rows=None, tile_map_ref=None, label=""):
     return err
 
 
-def sample_rows(prob, per_tile=2, seed=0):
-    """A few rows per 128-row tile (first and last of each tile plus random ones)."""
+# Row offsets inside each 16-row fragment band of a 128-row tile: band b takes a row from its
+# lower (0) or upper (1) half so that the eight rows fall in all eight classes of (r >> 3) & 7,
+# the row classes of the kernels' A-scale staging swizzle.
+_BAND_HALF = (0, 1, 0, 1, 1, 0, 1, 0)
+
+
+def sample_rows(prob, per_tile=12, seed=0):
+    """Rows of every 128-row tile to compare: the first and the last, one row in each of the
+    tile's eight 16-row fragment bands (a random row of the half given by ``_BAND_HALF``, so the
+    eight rows cover every A-scale swizzle class), and ``per_tile - 10`` random rows."""
     rng = np.random.default_rng(seed)
     rows = []
     for t in range(0, prob.M, 128):
         hi = min(t + 128, prob.M)
-        rows += [t, hi - 1] + list(rng.integers(t, hi, size=max(per_tile - 2, 0)))
+        cand = [t, hi - 1]
+        cand += [t + 16 * b + 8 * h + int(rng.integers(0, 8)) for b, h in enumerate(_BAND_HALF)]
+        cand += [int(r) for r in rng.integers(t, hi, size=max(per_tile - 10, 0))]
+        rows += [r for r in cand if r < hi]
     return np.unique(rows)
