@@ -68,40 +68,68 @@ constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;             // 4
 constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;             // 4
 constexpr int AS_INSTR = AS_BYTES / 256 / NWAVES;            // 4 (4-byte copies, 64 lanes)
 
-struct LoadPlan {
-  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, bs_rsrc, as_rsrc;
-  uint32_t voff[A_INSTR];    // A copies: per-lane offset of instruction i
-  uint32_t voff_b[B_INSTR];  // B copies: the same with B's rows permuted (see b_col)
-  uint32_t as_vrow;      // A scale chunk: lane part of the row offset
-  uint32_t as_row8;      // A scale chunk: bytes of 8 rows of a_scales
-  int a_dst, b_dst;
+// Buffer resources of one unit of work (one pass of a work item over its rows): A rows, the
+// expert's B rows of the column block, this wave's B scales and the A scales of the rows. A unit
+// that does not exist gets resources of zero bytes: copies through them read zeros and touch no
+// memory.
+struct UnitRsrc {
+  __amdgpu_buffer_rsrc_t a, b, bs, as;
 };
 
-// Copy i (of A_INSTR / B_INSTR per wave) of K block kb into the A or B half of a stage, and the
-// B scales of kb (waves 0 and 1, one column block each).
-__device__ __forceinline__ void copy_a(uint8_t* __restrict__ da, const LoadPlan& lp, int kb, int i) {
-  buf2lds16(lp.a_rsrc, lp.voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
-            as_lds(da + lp.a_dst + i * 1024));
+// Per-lane parts of the copies. They depend only on the lane, the wave and K, so every unit of
+// a workgroup shares them.
+struct CopyPlan {
+  uint32_t voff[A_INSTR];    // A copies: per-lane offset of instruction i
+  uint32_t voff_b[B_INSTR];  // B copies: the same with B's rows permuted (see b_col)
+  uint32_t as_vrow;          // A scale chunk: lane part of the row offset
+  uint32_t as_row8;          // A scale chunk: bytes of 8 rows of a_scales
+};
+
+// LDS destinations are passed as 32-bit LDS addresses (wave base + constant): see LdsBases.
+__device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(size_t)a; }
+
+// Copy i (of A_INSTR / B_INSTR per wave) of K block kb to LDS address dst (the stage's A or B
+// half plus this wave's part, see LdsBases), and the B scales of kb (waves 0 and 1, one column
+// block each).
+__device__ __forceinline__ void copy_a(uint32_t dst, __amdgpu_buffer_rsrc_t r, const CopyPlan& cp, int kb, int i) {
+  buf2lds16(r, cp.voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK, lds_ptr(dst + i * 1024));
 }
-__device__ __forceinline__ void copy_b(uint8_t* __restrict__ db, const LoadPlan& lp, int kb, int i) {
-  buf2lds16(lp.b_rsrc, lp.voff_b[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK,
-            as_lds(db + lp.b_dst + i * 1024));
+__device__ __forceinline__ void copy_b(uint32_t dst, __amdgpu_buffer_rsrc_t r, const CopyPlan& cp, int kb, int i) {
+  buf2lds16(r, cp.voff_b[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * BK, lds_ptr(dst + i * 1024));
 }
-__device__ __forceinline__ void copy_bs(uint8_t* __restrict__ dbs, const LoadPlan& lp, int kb, int wave) {
-  if (wave < 2)
-    buf2lds4(lp.bs_rsrc, 0, (uint32_t)__builtin_amdgcn_readfirstlane(kb) * 4, as_lds(dbs + wave * 256));
+__device__ __forceinline__ void copy_bs(uint32_t dst, __amdgpu_buffer_rsrc_t r, int kb, int wave) {
+  if (wave < 2) buf2lds4(r, 0, (uint32_t)__builtin_amdgcn_readfirstlane(kb) * 4, lds_ptr(dst));
 }
 
-__device__ __forceinline__ void issue_scale_chunk(uint8_t* __restrict__ dst, const LoadPlan& lp,
-                                                  int chunk, int wave) {
-  const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * AS_CHUNK * 4;
-  const uint32_t slot = threadIdx.x & 7;
-  // instruction i of wave w fills rows 32 w + 8 i + (lane >> 3); slot (lane & 7) of such a row
-  // holds column slot ^ ((4 w + i) & 7)
+__device__ __forceinline__ void issue_scale_chunk(uint32_t dst, __amdgpu_buffer_rsrc_t r,
+                                                  const CopyPlan& cp, int chunk, int wave) {
+  // Instruction i of wave w fills rows 32 w + 8 i + (lane >> 3); slot (lane & 7) of such a row
+  // holds column slot ^ ((4 w + i) & 7) = (slot ^ 4 (w & 1)) ^ i. The per-lane offsets are formed
+  // here from as_vrow (an empty asm keeps the compiler from hoisting all four out of the loop).
+  uint32_t v = cp.as_vrow + (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * AS_CHUNK * 4;
+  uint32_t sl = (threadIdx.x & 7) ^ (4 * (wave & 1));
+  asm volatile("" : "+v"(v), "+v"(sl));
 #pragma unroll
   for (int i = 0; i < AS_INSTR; i++)
-    buf2lds4(lp.as_rsrc, lp.as_vrow + i * lp.as_row8 + col + ((slot ^ ((4 * wave + i) & 7)) << 2), 0,
-             as_lds(dst + (wave * AS_INSTR + i) * 256));
+    buf2lds4(r, v + i * cp.as_row8 + ((sl ^ i) << 2), 0, lds_ptr(dst + i * 256));
+}
+
+// This wave's LDS copy destinations: wb + region offset for A and B (a wave fills 4 KiB of each
+// half), wbs for its B scale (waves 0 and 1), wch + buffer offset for its A scale rows. They are
+// re-derived through an empty asm at every K block so that the compiler forms each destination
+// (base + constant) next to its copy instead of keeping every combination live in SGPRs.
+struct LdsBases {
+  uint32_t wb, wbs, wch;
+};
+
+__device__ __forceinline__ LdsBases lds_bases(const uint8_t* smem, int wave) {
+  const uint32_t s0 = (uint32_t)(size_t)as_lds(const_cast<uint8_t*>(smem));
+  LdsBases l;
+  l.wb = s0 + wave * A_INSTR * 1024;
+  l.wbs = s0 + BS_REGION + wave * 256;
+  l.wch = s0 + AS_REGION + wave * AS_INSTR * 256;
+  asm volatile("" : "+s"(l.wb), "+s"(l.wbs), "+s"(l.wch));
+  return l;
 }
 
 __device__ __forceinline__ v8i read_frag(const uint8_t* p, const int (&base)[2]) {
@@ -126,39 +154,118 @@ __device__ __forceinline__ int b_col(int l) {
   return ((j >> 1) << 5) | (q << 3) | ((j & 1) << 2) | i;
 }
 
+// The tile map, from kernel arguments declared __restrict__ so that the compiler may read it with
+// scalar loads (counted apart from the copies in flight, which a vector load's wait would drain).
+struct TileMap {
+  const int32_t* expert_ids;
+  const int32_t* tile_offsets;
+};
+
+// One pass of a work item: rows [row0, row0 + rows) of expert e against columns [n0, n0 + 256).
+struct Unit {
+  int e, row0, rows, n0;
+};
+
+// The passes of work item L (super-tile L / n_blocks, column block L % n_blocks): one 256-row pass
+// when its two 128-row tiles are consecutive full rows of one expert, else one pass per live tile.
+// Returns the number of passes (0 when both tiles are skipped).
+__device__ __forceinline__ int item_units(const GemmArgs& p, const TileMap& tm, int n_blocks, int L, Unit (&u)[2]) {
+  const int s = L / n_blocks, n0 = (L % n_blocks) * BN;
+  const TileRows t0 = tile_rows(tm.expert_ids, tm.tile_offsets, 2 * s, p.M, TILE_M, p.num_experts);
+  TileRows t1 = {0, 0, 0};
+  if (2 * s + 1 < p.num_tiles)
+    t1 = tile_rows(tm.expert_ids, tm.tile_offsets, 2 * s + 1, p.M, TILE_M, p.num_experts);
+  u[0] = {t0.expert, t0.row0, t0.rows, n0};
+  u[1] = {t1.expert, t1.row0, t1.rows, n0};
+  if (t0.rows == TILE_M && t1.rows > 0 && t1.expert == t0.expert && t1.row0 == t0.row0 + TILE_M) {
+    u[0].rows = TILE_M + t1.rows;
+    return 1;
+  }
+  if (t0.rows > 0) return t1.rows > 0 ? 2 : 1;
+  u[0] = u[1];
+  return t1.rows > 0 ? 1 : 0;
+}
+
+// The units of one workgroup, in order: items xb, xb + G, xb + 2 G, ... (G = grid size), each
+// item's passes in turn. L is the current item, k the index of the next pass to take from it.
+struct UnitSeq {
+  int L, k;
+};
+
+__device__ __forceinline__ bool next_unit(const GemmArgs& p, const TileMap& tm, int n_blocks, int items,
+                                          UnitSeq& q, Unit& out) {
+  Unit u[2];
+  int n = q.L < 0 ? 0 : item_units(p, tm, n_blocks, q.L, u);
+  while (q.k >= n) {
+    q.L += gridDim.x;
+    if (q.L >= items) return false;
+    n = item_units(p, tm, n_blocks, q.L, u);
+    q.k = 0;
+  }
+  out = q.k == 0 ? u[0] : u[1];
+  q.k++;
+  out.e = __builtin_amdgcn_readfirstlane(out.e);
+  out.row0 = __builtin_amdgcn_readfirstlane(out.row0);
+  out.rows = __builtin_amdgcn_readfirstlane(out.rows);
+  out.n0 = __builtin_amdgcn_readfirstlane(out.n0);
+  return true;
+}
+
+// Resources of unit u (zero bytes when !live): rows past the unit (ragged M), columns past N
+// and scales past a_scales read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_a(const GemmArgs& p, const Unit& u, bool live) {
+  const size_t K = (size_t)p.K;
+  return make_rsrc((const uint8_t*)p.A + (size_t)u.row0 * K, live ? (uint64_t)u.rows * K : 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const GemmArgs& p, const Unit& u, bool live) {
+  const size_t K = (size_t)p.K;
+  return make_rsrc((const uint8_t*)p.B + ((size_t)u.e * p.N + u.n0) * K,
+                   live ? (uint64_t)min(BN, p.N - u.n0) * K : 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bs(const GemmArgs& p, const Unit& u, bool live, int wave) {
+  const int N = p.N, KB = p.K / BK;
+  const int cb = min(u.n0 / 128 + (wave & 1), N / 128 - 1);    // wave 0 / 1: column block 0 / 1
+  return make_rsrc((const float*)p.b_scales + ((size_t)u.e * (N / 128) + cb) * KB, live ? (uint64_t)KB * 4 : 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_as(const GemmArgs& p, const Unit& u, bool live) {
+  const int KB = p.K / BK;
+  return make_rsrc((const float*)p.a_scales + (size_t)u.row0 * KB, live ? (uint64_t)u.rows * KB * 4 : 0);
+}
+
 template <int OUT>
-__global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p, int n_blocks) {
+__global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p, int n_blocks,
+                                                                       const int32_t* __restrict__ expert_ids,
+                                                                       const int32_t* __restrict__ tile_offsets,
+                                                                       void* __restrict__ C) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  const TileMap tm = {expert_ids, tile_offsets};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int num_super = (p.num_tiles + 1) / 2;
-  int s, nb;
-  if (!work_item(num_super, n_blocks, 1, s, nb)) return;
-  const int n0 = nb * BN, N = p.N, KB = p.K / BK;
+  const int items = ((p.num_tiles + 1) / 2) * n_blocks;
+  const int N = p.N, KB = p.K / BK;
   const size_t K = (size_t)p.K;
   const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
   const int r16 = lane & 15, q = lane >> 4;
-  const int ncols = min(BN, N - n0);
+  // Consecutive K blocks of the units of this workgroup share one pipeline: the last blocks of a
+  // unit copy the first blocks (and A scale chunks) of the next, so a unit after the first has
+  // no prologue and its output stores drain under the next unit's first passes. This needs an
+  // even number of K blocks (block 0 of every unit in stage 0); with an odd number each unit
+  // starts with its own prologue.
+  const bool piped = (KB & 1) == 0;
+  const int nchunks = (KB + AS_CHUNK - 1) / AS_CHUNK;
 
-  // The two 128-row tiles of this super-tile: one 256-row pass when they are consecutive rows
-  // of one expert, else one pass per tile.
-  const TileRows t0 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s, p.M, TILE_M, p.num_experts);
-  TileRows t1 = {0, 0, 0};
-  if (2 * s + 1 < p.num_tiles)
-    t1 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s + 1, p.M, TILE_M, p.num_experts);
-  // pass 0 is (e0, r0, n0rows), pass 1 (if any) is (e1, r1, n1rows); all block-uniform
-  int e0 = t0.expert, r0 = t0.row0, n0rows = t0.rows, e1 = t1.expert, r1 = t1.row0, n1rows = t1.rows;
-  int npass;
-  if (t0.rows == TILE_M && t1.rows > 0 && t1.expert == t0.expert && t1.row0 == t0.row0 + TILE_M) {
-    n0rows = TILE_M + t1.rows;
-    npass = 1;
-  } else if (t0.rows > 0) {
-    npass = t1.rows > 0 ? 2 : 1;
-  } else {
-    e0 = e1; r0 = r1; n0rows = n1rows;
-    npass = t1.rows > 0 ? 1 : 0;
-  }
+  // Work order: the grid is a multiple of 8 and blocks are dispatched round-robin over the 8
+  // XCDs, so block b runs on XCD b % 8. In each round of G = grid items, the blocks of one XCD
+  // take a contiguous run of G / 8 items; items walk one super-tile across all its column blocks
+  // before the next, so those in flight on an XCD share A rows (and, across its two super-tiles,
+  // B columns) in its L2.
+  UnitSeq seq;
+  seq.L = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 - gridDim.x;
+  seq.k = 0;
+  Unit cu, nx;
+  if (!next_unit(p, tm, n_blocks, items, seq, cu)) return;
+  bool have_next = next_unit(p, tm, n_blocks, items, seq, nx);
 
   // per-lane LDS read bases: lane (r16, q) holds K bytes [32 q, 32 q + 32) of row r16 of a
   // fragment (two 16-byte chunks); the swizzle of row 16 f + r16 depends on r16 only
@@ -175,39 +282,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
   const int base_as = (AS_REGION + (wm * WM + r16) * AS_CHUNK * 4) | ((r16 >> 3) << 2);
   const int base_bs = BS_REGION + wn * 256;
 
-  for (int ps = 0; ps < npass; ps++) {
-    const int e = __builtin_amdgcn_readfirstlane(ps == 0 ? e0 : e1);
-    const int row0 = __builtin_amdgcn_readfirstlane(ps == 0 ? r0 : r1);
-    const int rows = __builtin_amdgcn_readfirstlane(ps == 0 ? n0rows : n1rows);
-    const uint8_t* A = (const uint8_t*)p.A;
-    const uint8_t* Be = (const uint8_t*)p.B + (size_t)e * N * K;
-
-    // Copy plan. Rows past the pass (ragged M) or past N read as zero through the resource
-    // bounds; so do scales past the end of a_scales.
-    LoadPlan lp;
-    lp.a_rsrc = make_rsrc(A + (size_t)row0 * K, (uint64_t)rows * K);
-    lp.b_rsrc = make_rsrc(Be + (size_t)n0 * K, (uint64_t)ncols * K);
-    {
-      const int cb = min(n0 / 128 + (wave & 1), N / 128 - 1);    // wave 0 / 1: column block 0 / 1
-      lp.bs_rsrc = make_rsrc((const float*)p.b_scales + ((size_t)e * (N / 128) + cb) * KB, (uint64_t)KB * 4);
-    }
-    lp.as_rsrc = make_rsrc((const float*)p.a_scales + (size_t)row0 * KB, (uint64_t)rows * KB * 4);
-    {
-      const int lrow = lane >> 3, slot = lane & 7;
-      // Instruction i of wave w covers rows 32 w + 8 i + lrow (swz8 of that row is lrow ^ (i & 1)).
-      // The whole row offset sits in the per-lane offset, which the resource bounds check.
+  CopyPlan cp;
+  {
+    const int lrow = lane >> 3, slot = lane & 7;
+    // Instruction i of wave w covers LDS rows 32 w + 8 i + lrow (swz8 of that row is
+    // lrow ^ (i & 1)). The whole row offset sits in the per-lane offset, which the resource
+    // bounds check.
 #pragma unroll
-      for (int i = 0; i < A_INSTR; i++) {
-        const int l = wave * 32 + i * 8 + lrow;  // LDS row
-        const uint32_t chunk = (uint32_t)((slot ^ lrow ^ (i & 1)) * 16);
-        lp.voff[i] = (uint32_t)(l * K) + chunk;
-        lp.voff_b[i] = (uint32_t)(((l & 128) | b_col(l & 127)) * K) + chunk;
-      }
-      lp.a_dst = wave * A_INSTR * 1024;
-      lp.b_dst = wave * B_INSTR * 1024;
-      // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow
-      lp.as_vrow = (uint32_t)((wave * 32 + lrow) * KB * 4);
-      lp.as_row8 = (uint32_t)(8 * KB * 4);
+    for (int i = 0; i < A_INSTR; i++) {
+      const int l = wave * 32 + i * 8 + lrow;
+      const uint32_t chunk = (uint32_t)((slot ^ lrow ^ (i & 1)) * 16);
+      cp.voff[i] = (uint32_t)(l * K) + chunk;
+      cp.voff_b[i] = (uint32_t)(((l & 128) | b_col(l & 127)) * K) + chunk;
+    }
+    // A scale chunk: instruction i of wave w covers rows 32 w + 8 i + lrow
+    cp.as_vrow = (uint32_t)((wave * 32 + lrow) * KB * 4);
+    cp.as_row8 = (uint32_t)(8 * KB * 4);
+  }
+
+  int cbase = 0;   // A scale buffer of the current unit's chunk 0; chunk c is in buffer (cbase + c) & 1
+  // The copy resources. Piped, each switches from the current unit to the next at the block
+  // from which its copies only target the next unit (B: block KB-2, A and B scales: KB-1,
+  // A scales: the block that loads the next unit's first chunk), so at a unit's start they
+  // already describe it.
+  UnitRsrc rc;
+  for (bool first = true;; first = false) {
+    const int rows = cu.rows, row0 = cu.row0, n0 = cu.n0;
+    const bool nx_live = have_next && piped;
+
+    if (first || !piped) {
+      // prologue: A scales of chunks 0 and 1, block 0 and the B half of block 1 (its A half and
+      // B scales go out in passes 0 and 1 of block 0, as in every block); block 0 published
+      if (!first) barrier();     // every wave is past its last LDS read of the previous unit
+      cbase = 0;
+      rc.a = rsrc_a(p, cu, true);
+      rc.b = rsrc_b(p, cu, true);
+      rc.bs = rsrc_bs(p, cu, true, wave);
+      rc.as = rsrc_as(p, cu, true);
+      const LdsBases lb = lds_bases(smem, wave);
+      issue_scale_chunk(lb.wch, rc.as, cp, 0, wave);
+      issue_scale_chunk(lb.wch + AS_BYTES, rc.as, cp, 1, wave);
+#pragma unroll
+      for (int i = 0; i < A_INSTR; i++) copy_a(lb.wb + A_REGION, rc.a, cp, 0, i);
+#pragma unroll
+      for (int i = 0; i < B_INSTR; i++) copy_b(lb.wb + B_REGION, rc.b, cp, 0, i);
+      copy_bs(lb.wbs, rc.bs, 0, wave);
+#pragma unroll
+      for (int i = 0; i < B_INSTR; i++) copy_b(lb.wb + B_REGION + B_BYTES, rc.b, cp, min(1, KB - 1), i);
+      wait_vmcnt<0>();
+      barrier();
     }
 
     v4f acc[MI][NJ];
@@ -216,21 +339,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: A scales of chunks 0 and 1, block 0 and the B half of block 1 (its A half and B
-    // scales go out in passes 0 and 1 of block 0, as in every block); block 0 published
-    issue_scale_chunk(smem + AS_REGION, lp, 0, wave);
-    issue_scale_chunk(smem + AS_REGION + AS_BYTES, lp, 1, wave);
-#pragma unroll
-    for (int i = 0; i < A_INSTR; i++) copy_a(smem + A_REGION, lp, 0, i);
-#pragma unroll
-    for (int i = 0; i < B_INSTR; i++) copy_b(smem + B_REGION, lp, 0, i);
-    copy_bs(smem + BS_REGION, lp, 0, wave);
-#pragma unroll
-    for (int i = 0; i < B_INSTR; i++) copy_b(smem + B_REGION + B_BYTES, lp, min(1, KB - 1), i);
-    wait_vmcnt<0>();
-    barrier();
-
-    // The K loop, in two forms. A wave whose 64 rows all lie past the pass's rows (the upper half
+    // The K loop, in two forms. A wave whose 64 rows all lie past the unit's rows (the upper half
     // of a 128-row pass) runs it without reads, MFMAs or promotion: it still issues its copies
     // and reaches every barrier, so both forms keep the same sequence of waits and barriers.
     auto k_loop = [&](auto active_tag) {
@@ -239,19 +348,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     float as_raw[MI], bs_raw = 0.f;
     if constexpr (ACT) {
 #pragma unroll
-    for (int i = 0; i < MI; i++) af[i] = read_frag(smem + i * 2048, base_a);
-    bq[0] = read_frag(smem, base_b);
-    bq[1] = read_frag(smem + 2048, base_b);
+      for (int i = 0; i < MI; i++) af[i] = read_frag(smem + i * 2048, base_a);
+      bq[0] = read_frag(smem, base_b);
+      bq[1] = read_frag(smem + 2048, base_b);
+      const int as0 = base_as + (cbase & 1) * AS_BYTES;
 #pragma unroll
-    for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + (base_as ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
-    bs_raw = *(const float*)(smem + base_bs);
+      for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + (as0 ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
+      bs_raw = *(const float*)(smem + base_bs);
     }
 
-    for (int b = 0; b < KB; b++) {
-      const int S = b & 1;
-      const int so_ab = S * A_BYTES;                               // this block's stage
-      [[maybe_unused]] const int so_bs = S * BS_BYTES;
-      const int sn_ab = (S ^ 1) * A_BYTES, sn_bs = (S ^ 1) * BS_BYTES;
+    // One K block. S (its stage) is a constant so every LDS offset is an immediate. Blocks of the
+    // main loop (TAIL false) copy from the current unit only; the last two blocks (TAIL true)
+    // copy the next unit's first blocks when piped, else repeat block KB-1 into a stage that is
+    // not read again.
+    auto k_block = [&](auto stage_tag, auto tail_tag, const int b) {
+      constexpr int S = decltype(stage_tag)::value;
+      constexpr bool TAIL = decltype(tail_tag)::value;
+      constexpr int so_ab = S * A_BYTES, sn_ab = (S ^ 1) * A_BYTES;   // this and the other stage
+      constexpr int sn_bs = (S ^ 1) * BS_BYTES;
+      // copy targets: the A half and B scales of block b+1, the B half of block b+2
+      int kb_a = b + 1, kb_b = min(b + 2, KB - 1);
+      if constexpr (TAIL) {
+        if (piped) {
+          kb_b = b + 2 - KB;
+          if (b == KB - 1) {
+            kb_a = 0;
+            rc.a = rsrc_a(p, nx, nx_live);
+            rc.bs = rsrc_bs(p, nx, nx_live, wave);
+          }
+        } else {
+          kb_a = min(b + 1, KB - 1);
+        }
+      }
+      const LdsBases lb = lds_bases(smem, wave);
       float sc[MI];
       if constexpr (ACT) {
 #pragma unroll
@@ -281,8 +410,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
             }
           }
           if (j < 2 && (i & 1)) {
-            copy_a(smem + A_REGION + sn_ab, lp, min(b + 1, KB - 1), 2 * j + (i >> 1));
-            if (j == 1 && i == 3) copy_bs(smem + BS_REGION + sn_bs, lp, min(b + 1, KB - 1), wave);
+            copy_a(lb.wb + A_REGION + sn_ab, rc.a, cp, kb_a, 2 * j + (i >> 1));
+            if (j == 1 && i == 3) copy_bs(lb.wbs + sn_bs, rc.bs, kb_a, wave);
           }
           if constexpr (ACT) {
             if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[0]);
@@ -301,10 +430,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       wait_vmcnt<0>();
       wait_lds_reads();
       barrier();
+      if constexpr (TAIL) {
+        if (piped && b == KB - 2) rc.b = rsrc_b(p, nx, nx_live);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // pass 6 (B fragment 6, no reads left in this block) with copies 0 and 1 of the B half of
-      // block b+2 into stage S (past the last block, copies repeat block KB-1 into a stage that is
-      // not read again)
+      // block b+2 into stage S
 #pragma unroll
       for (int i = 0; i < MI; i++) {
         const int k = (NJ - 2) * MI + i;
@@ -314,12 +445,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           acc[ip][jp] += part[kp % 4] * sc[ip];
           asm volatile("" : "+v"(acc[ip][jp]));
         }
-        if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), i >> 1);
+        if (i & 1) copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, i >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (b % AS_CHUNK == 0 && b > 0)
-        issue_scale_chunk(smem + AS_REGION + ((b / AS_CHUNK + 1) & 1) * AS_BYTES, lp, b / AS_CHUNK + 1,
-                          wave);
+      // A scale chunks. Chunk c (blocks 8c .. 8c+7) goes into its buffer in block 8(c-1), when
+      // the buffer's previous chunk (c-2) has been read by every wave. Chunks 0 and 1 of a unit
+      // are loaded before it starts: in its prologue, or piped in the previous unit's blocks
+      // KB-2 and KB-1 (chunk 0's buffer held chunk n-2 of that unit, n = chunks per unit, and
+      // chunk 1's its last chunk, read for the last time before the barrier of block KB-1).
+      if constexpr (!TAIL && S == 0) {
+        if (b % AS_CHUNK == 0 && b > 0 && b / AS_CHUNK + 1 < nchunks) {
+          const int c = b / AS_CHUNK + 1;
+          issue_scale_chunk(lb.wch + ((cbase + c) & 1) * AS_BYTES, rc.as, cp, c, wave);
+        }
+      }
+      if constexpr (TAIL) {
+        if (piped && b == KB - 2) {
+          rc.as = rsrc_as(p, nx, nx_live);
+          issue_scale_chunk(lb.wch + ((cbase + nchunks) & 1) * AS_BYTES, rc.as, cp, 0, wave);
+        }
+        if (piped && b == KB - 1)
+          issue_scale_chunk(lb.wch + ((cbase + nchunks + 1) & 1) * AS_BYTES, rc.as, cp, 1, wave);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
       // MFMA, then the first two B fragments and the scales of block b+1 are read; copies 2 and 3
@@ -334,14 +481,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           asm volatile("" : "+v"(acc[ip][jp]));
           af[i] = read_frag(smem + sn_ab + i * 2048, base_a);
         }
-        if (i & 1) copy_b(smem + B_REGION + so_ab, lp, min(b + 2, KB - 1), 2 + (i >> 1));
+        if (i & 1) copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, 2 + (i >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (ACT) {
         bq[0] = read_frag(smem + sn_ab, base_b);
         bq[1] = read_frag(smem + sn_ab + 2048, base_b);
         const int bn = min(b + 1, KB - 1);
-        const int as_v = (base_as ^ ((bn % AS_CHUNK) * 4)) + ((bn / AS_CHUNK) & 1) * AS_BYTES;
+        const int as_v = (base_as ^ ((bn % AS_CHUNK) * 4)) + ((cbase + bn / AS_CHUNK) & 1) * AS_BYTES;
 #pragma unroll
         for (int i = 0; i < MI; i++)
           as_raw[i] = *(const float*)(smem + (as_v ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
@@ -357,16 +504,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           asm volatile("" : "+v"(acc[ip][jp]));
         }
       }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    int b = 0;
+    for (; b + 2 < KB; b += 2) {
+      k_block(S0{}, std::false_type{}, b);
+      k_block(S1{}, std::false_type{}, b + 1);
     }
+    // KB even: blocks KB-2 (stage 0) and KB-1 (stage 1); KB odd: block KB-1 (stage 0)
+    k_block(S0{}, std::true_type{}, b);
+    if (b + 1 < KB) k_block(S1{}, std::true_type{}, b + 1);
     };
     if (wm * WM < rows)
       k_loop(std::true_type{});
     else
       k_loop(std::false_type{});
-    wait_vmcnt<0>();
 
     // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
-    // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col)
+    // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col). The stores are
+    // not waited for: the next unit's first wait before a barrier covers them.
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       const int mloc = wm * WM + i * 16 + r16;
@@ -375,10 +533,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 #pragma unroll
       for (int jj = 0; jj < NJ / 2; jj++) {
         const int col = n0 + wn * WN + jj * 32 + q * 8;
-        if (col < N) store8<OUT>(p.C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
+        if (col < N) store8<OUT>(C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
       }
     }
-    if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass
+    if (!have_next) break;
+    cbase = (cbase + nchunks) & 1;
+    cu = nx;
+    have_next = next_unit(p, tm, n_blocks, items, seq, nx);
   }
 }
 
@@ -386,14 +547,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
 
 hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream) {
   const int n_blocks = (a.N + BN - 1) / BN;
-  const long long blocks = (long long)((a.num_tiles + 1) / 2) * n_blocks;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7ffffff0LL) return hipErrorInvalidValue;
-  dim3 grid(grid_for(blocks)), block(NTHREADS);
+  const long long items = (long long)((a.num_tiles + 1) / 2) * n_blocks;
+  if (items == 0) return hipSuccess;
+  if (items > 0x7ffffff0LL) return hipErrorInvalidValue;
+  // persistent grid: one workgroup per compute unit (the LDS ring allows one), fewer when there
+  // are fewer items; a multiple of 8 for the XCD-aware order
+  dim3 grid(grid_for(items < a.num_cus ? items : a.num_cus)), block(NTHREADS);
   switch (out) {
-    case kOutF32: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutF32>, grid, block, 0, stream, a, n_blocks); break;
-    case kOutBF16: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutBF16>, grid, block, 0, stream, a, n_blocks); break;
-    case kOutF16: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutF16>, grid, block, 0, stream, a, n_blocks); break;
+    case kOutF32: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutF32>, grid, block, 0, stream, a, n_blocks, a.expert_ids, a.tile_offsets, a.C); break;
+    case kOutBF16: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutBF16>, grid, block, 0, stream, a, n_blocks, a.expert_ids, a.tile_offsets, a.C); break;
+    case kOutF16: hipLaunchKernelGGL(bw_fp8_grouped_kernel<kOutF16>, grid, block, 0, stream, a, n_blocks, a.expert_ids, a.tile_offsets, a.C); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -14,15 +14,18 @@ namespace {
 constexpr int kMaxDevices = 64;
 // per-device cache: 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_num_cus[kMaxDevices];
 
-int check_device() {
+// Checks that the current device is a gfx950; on success stores its compute-unit count in
+// *num_cus (if given).
+int check_device(int* num_cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return BSG_ERR_DEVICE;
   }
   if (dev >= kMaxDevices) return BSG_ERR_DEVICE;
-  int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+  int known = g_arch_ok[dev].load(std::memory_order_acquire);
   if (known == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -30,8 +33,11 @@ int check_device() {
       return BSG_ERR_DEVICE;
     }
     known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_arch_ok[dev].store(known, std::memory_order_relaxed);
+    g_num_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                         std::memory_order_relaxed);
+    g_arch_ok[dev].store(known, std::memory_order_release);
   }
+  if (num_cus) *num_cus = g_num_cus[dev].load(std::memory_order_relaxed);
   return known == 1 ? BSG_OK : BSG_ERR_DEVICE;
 }
 
@@ -132,7 +138,8 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
       !aligned(b_scales, scale_align) || (!dense && (!aligned(expert_ids, 4) || !aligned(tile_offsets, 4))))
     return BSG_ERR_ALIGN;
   if (M == 0 || (!dense && num_tiles == 0)) return BSG_OK;
-  if (int st = check_device()) return st;
+  int num_cus = 0;
+  if (int st = check_device(&num_cus)) return st;
 
   bsg::GemmArgs args;
   args.A = A;
@@ -147,6 +154,7 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
   args.K = K;
   args.num_experts = dense ? 1 : num_experts;
   args.num_tiles = dense ? (M + 127) / 128 : num_tiles;
+  args.num_cus = num_cus;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (sk == BSG_SCALE_BLOCKWISE)

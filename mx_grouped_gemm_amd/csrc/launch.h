@@ -17,6 +17,7 @@ struct GemmArgs {
   int M, N, K;
   int num_experts;
   int num_tiles;  // M-tiles of 128 rows to visit
+  int num_cus;    // compute units of the device (size of a persistent grid)
 };
 
 // Blockwise-FP8 (e4m3 x e4m3, fp32 1x128 / 128x128 scales). out: 1 f32, 2 bf16, 3 f16.
