@@ -65,17 +65,18 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
 // touch 16 different 16-byte bank groups.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Output conversions (round to nearest even).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Output conversions (round to nearest even). A pair of fp32 values becomes one dword of two
+// bf16 (gfx950 converts a pair in one instruction, v_cvt_pk_bf16_f32) or two fp16.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t){lo, hi}, v2bf_t));
 }
 __device__ __forceinline__ uint32_t f16_bits(float f) {
   _Float16 h = (_Float16)f;
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
+__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) { return f16_bits(lo) | (f16_bits(hi) << 16); }
 
 enum OutKind { kOutF32 = 1, kOutBF16 = 2, kOutF16 = 3 };
 
@@ -87,13 +88,13 @@ __device__ __forceinline__ void store4(void* C, size_t off, float a, float b, fl
                                      (int)__float_as_uint(c), (int)__float_as_uint(d)};
   } else if constexpr (OUT == kOutBF16) {
     uint2 v;
-    v.x = bf16_bits(a) | (bf16_bits(b) << 16);
-    v.y = bf16_bits(c) | (bf16_bits(d) << 16);
+    v.x = bf16x2_bits(a, b);
+    v.y = bf16x2_bits(c, d);
     *(uint2*)((uint16_t*)C + off) = v;
   } else {
     uint2 v;
-    v.x = f16_bits(a) | (f16_bits(b) << 16);
-    v.y = f16_bits(c) | (f16_bits(d) << 16);
+    v.x = f16x2_bits(a, b);
+    v.y = f16x2_bits(c, d);
     *(uint2*)((uint16_t*)C + off) = v;
   }
 }
@@ -107,10 +108,9 @@ __device__ __forceinline__ void store8(void* C, size_t off, const float __attrib
     store4<OUT>(C, off, lo[0], lo[1], lo[2], lo[3]);
     store4<OUT>(C, off + 4, hi[0], hi[1], hi[2], hi[3]);
   } else {
-    uint32_t (*cv)(float) = OUT == kOutBF16 ? bf16_bits : f16_bits;
-    *(v4i*)((uint16_t*)C + off) =
-        (v4i){(int)(cv(lo[0]) | (cv(lo[1]) << 16)), (int)(cv(lo[2]) | (cv(lo[3]) << 16)),
-              (int)(cv(hi[0]) | (cv(hi[1]) << 16)), (int)(cv(hi[2]) | (cv(hi[3]) << 16))};
+    uint32_t (*cv)(float, float) = OUT == kOutBF16 ? bf16x2_bits : f16x2_bits;
+    *(v4i*)((uint16_t*)C + off) = (v4i){(int)cv(lo[0], lo[1]), (int)cv(lo[2], lo[3]),
+                                        (int)cv(hi[0], hi[1]), (int)cv(hi[2], hi[3])};
   }
 }
 
