@@ -20,10 +20,11 @@ With --workload nvfp4_8192 a step is one dense nvfp4 GEMM of 8192^3 (e2m1 elemen
 scale per 16 K, fp16 out); the products run on the f16 matrix instruction, so its roofline is
 against the f16 peak.
 
-With --workload dense_4096 (one group 4096^3, every 64th row of A and B x100) or moe8_n2048_k4096
-(8 experts, 4096 tokens at top-2, Dirichlet(0.5), N=2048, K=4096) a step is the tile map (grouped
-only) and one blockwise-FP8 GEMM launch, bf16 out; its roofline is that launch against the FP8
-peak.
+With --workload dense_4096 (one group 4096^3, every 64th row of A and B x100), moe8_n2048_k4096
+(8 experts, 4096 tokens at top-2, Dirichlet(0.5), N=2048, K=4096) or dense_256x2048x16384 (8 work
+items with a long K) a step is the tile map (grouped only) and one blockwise-FP8 GEMM call, bf16
+out, through bsgemm_grouped_ws (its split-K schedule applies to the last one only; --no-split
+calls bsgemm_grouped); its roofline is that call against the FP8 peak.
 
 With --workload permute_moe32 a step is the step before the GEMM on the same routing: per-expert
 counts of the top-8 picks, the tile map, and the permutation of the 16384 bf16 token rows
@@ -99,7 +100,7 @@ def parse():
     ap.add_argument("--workload", default="moe32",
                     choices=["moe32", "mx8192_e4m3_e4m3", "mx8192_e4m3_e2m1", "mx8192_e2m1_e2m1",
                              "nvfp4_8192", "permute_moe32", "decode_moe32", "dense_4096",
-                             "moe8_n2048_k4096"])
+                             "moe8_n2048_k4096", "dense_256x2048x16384"])
     ap.add_argument("--mx-k", type=int, default=8192, metavar="K",
                     help="K of the mx8192_* and nvfp4_8192 workloads (M = N = 8192; the pages' "
                          "K sweep runs 512 .. 8192)")
@@ -107,6 +108,9 @@ def parse():
                     help="single-launch workloads: before each timed launch write 512 MiB of "
                          "scratch (untimed) so no operand is left in the caches; report the "
                          "median and minimum launch time")
+    ap.add_argument("--no-split", action="store_true",
+                    help="blockwise workloads: call bsgemm_grouped (whole work items only) instead of "
+                         "bsgemm_grouped_ws (the last rounds of work items split along K)")
     ap.add_argument("--sched-small-m", action="store_true",
                     help="dense_4096 / moe8_n2048_k4096: request the one-M-tile-per-item schedule")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -471,10 +475,18 @@ def bench_blockwise(args, torch, bsg, make_problem):
         to = torch.empty(T + 1, dtype=torch.int32, device=dev)
         ei = torch.empty(T, dtype=torch.int32, device=dev)
 
+    ws = None if args.no_split else torch.empty(bsg.bsgemm_grouped_workspace_size(), dtype=torch.uint8,
+                                                device=dev)
+
     def gemm():
-        bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei if grouped else None,
-                           to if grouped else None, C, p.M, p.N, p.K, fmt, num_tiles=T,
-                           num_experts=p.E, stream=stream)
+        if ws is None:
+            bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei if grouped else None,
+                               to if grouped else None, C, p.M, p.N, p.K, fmt, num_tiles=T,
+                               num_experts=p.E, stream=stream)
+        else:
+            bsg.bsgemm_grouped_ws(p.qa, p.a_scales, p.qb, p.b_scales, ei if grouped else None,
+                                  to if grouped else None, C, p.M, p.N, p.K, fmt, ws, num_tiles=T,
+                                  num_experts=p.E, stream=stream)
 
     def step():
         if grouped:
@@ -504,7 +516,9 @@ def bench_blockwise(args, torch, bsg, make_problem):
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
     desc = {"dense_4096": "one group 4096^3, every 64th row of A and B x100",
-            "moe8_n2048_k4096": "8 experts, 4096 tokens x top-2, Dirichlet(0.5), N=2048, K=4096"}
+            "moe8_n2048_k4096": "8 experts, 4096 tokens x top-2, Dirichlet(0.5), N=2048, K=4096",
+            "dense_256x2048x16384": "one group M=256, N=2048, K=16384 (8 work items, split along K "
+                                    "by bsgemm_grouped_ws)"}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2), "n_gpus": 1,
@@ -513,7 +527,8 @@ def bench_blockwise(args, torch, bsg, make_problem):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {desc[args.workload]}, blockwise e4m3 "
                                f"1x128/128x128 fp32 scales, bf16 out", "real_rows": p.real_rows,
-                   "padded_rows": p.M, "N": p.N, "K": p.K, "experts": p.E, "seed": args.seed},
+                   "padded_rows": p.M, "N": p.N, "K": p.K, "experts": p.E, "seed": args.seed,
+                   "entry_point": "bsgemm_grouped" if ws is None else "bsgemm_grouped_ws"},
         "kernels_ms": {"gemm": round(kernel_ms, 4)},
         **({"cold_ms": {"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4),
                         "tflops_at_median": round(flops / (np.median(cold) * 1e-3) / 1e12, 1)}}
@@ -584,7 +599,7 @@ def main():
     if args.workload == "decode_moe32":
         bench_decode(args, torch, bsg)
         return
-    if args.workload in ("dense_4096", "moe8_n2048_k4096"):
+    if args.workload in ("dense_4096", "moe8_n2048_k4096", "dense_256x2048x16384"):
         bench_blockwise(args, torch, bsg, make_problem)
         return
     if args.workload != "moe32":
@@ -606,6 +621,16 @@ def main():
     C_dn = torch.empty(dn.M, dn.N, dtype=torch.bfloat16, device=dev)
     fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
     stream = torch.cuda.current_stream()
+    ws = None if args.no_split else torch.empty(bsg.bsgemm_grouped_workspace_size(), dtype=torch.uint8,
+                                                device=dev)
+
+    def gemm(p, C):
+        if ws is None:
+            bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, expert_ids, tile_offsets, C, p.M, p.N,
+                               p.K, fmt, num_tiles=T, num_experts=p.E, stream=stream)
+        else:
+            bsg.bsgemm_grouped_ws(p.qa, p.a_scales, p.qb, p.b_scales, expert_ids, tile_offsets, C, p.M,
+                                  p.N, p.K, fmt, ws, num_tiles=T, num_experts=p.E, stream=stream)
 
     names = ("tile_map", "gate_up", "down")
     ev = {n: [] for n in names}
@@ -618,11 +643,9 @@ def main():
         a = mark() if record else None
         bsg.bsgemm_build_tiles(counts, T, True, expert_offsets, tile_offsets, expert_ids, stream)
         b = mark() if record else None
-        bsg.bsgemm_grouped(gu.qa, gu.a_scales, gu.qb, gu.b_scales, expert_ids, tile_offsets, C_gu,
-                           gu.M, gu.N, gu.K, fmt, num_tiles=T, num_experts=gu.E, stream=stream)
+        gemm(gu, C_gu)
         c = mark() if record else None
-        bsg.bsgemm_grouped(dn.qa, dn.a_scales, dn.qb, dn.b_scales, expert_ids, tile_offsets, C_dn,
-                           dn.M, dn.N, dn.K, fmt, num_tiles=T, num_experts=dn.E, stream=stream)
+        gemm(dn, C_dn)
         d = mark() if record else None
         if record:
             ev["tile_map"].append((a, b))
@@ -665,6 +688,7 @@ def main():
                         "(N=7168, K=2048), blockwise e4m3 1x128/128x128 fp32 scales, bf16 out",
             "experts": gu.E, "tokens": 16384, "top_k": 8, "real_rows": gu.real_rows,
             "padded_rows": gu.M, "m_tiles": T, "seed": args.seed,
+            "entry_point": "bsgemm_grouped" if ws is None else "bsgemm_grouped_ws",
         },
         "kernels_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
         "kernels_tflops": {"gate_up": round(gu_tflops, 1), "down": round(dn_tflops, 1)},

@@ -25,6 +25,7 @@
 #ifndef BSGEMM_H
 #define BSGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -144,6 +145,47 @@ int bsgemm_grouped(const void* A, const void* a_scales, const void* B, const voi
                    const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles,
                    void* C, int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
                    void* stream);
+
+/*
+ * bsgemm_grouped_workspace_size - bytes of workspace bsgemm_grouped_ws needs on the current device.
+ *
+ *   bytes   HOST size_t* (output): 4 KiB of flags plus one 256 x 256 fp32 tile per workgroup of
+ *           the split schedule (one per compute unit, rounded down to a multiple of 8: 64 MiB + 4 KiB
+ *           on a 256-CU MI355X)
+ * Errors: BSG_ERR_NULL, BSG_ERR_DEVICE.
+ */
+int bsgemm_grouped_workspace_size(size_t* bytes);
+
+/*
+ * bsgemm_grouped_ws - bsgemm_grouped with a workspace for a split-K schedule of small problems.
+ *
+ * Same operation, arguments and results as bsgemm_grouped (up to the rounding order of fp32 sums:
+ * outputs are within the same tolerance, not bit-identical). bsgemm_grouped runs one 256 x 256
+ * work item per workgroup, so a problem with fewer items than compute units leaves units idle
+ * (a 256 x 2048 x 16384 GEMM has 8 items for 256 units). With a workspace, such blockwise calls
+ * cut each item along K into 2-16 equal ranges of at least 8 K blocks (as many as the grid
+ * holds) that run side by side: each range accumulates its K blocks as described under
+ * bsgemm_grouped into an fp32 partial tile, and the item's result is the sum of its ranges'
+ * partials (each range sums and stores a slice of the tile). Problems with at least as many
+ * items as compute units, formats other than blockwise, and the small-M hint run exactly as
+ * bsgemm_grouped and leave the workspace untouched.
+ *
+ *   workspace        DEVICE, 256-byte aligned, at least bsgemm_grouped_workspace_size bytes,
+ *                    owned by the caller; no initial contents are required (its flags are
+ *                    cleared on the stream before each split launch). Its int32 word 1023 is
+ *                    an error word: nonzero after a call if a range ever stopped waiting for the
+ *                    other ranges of its item (not expected while the call has the GPU's compute
+ *                    units to itself; that item's output is then wrong).
+ *   workspace_bytes  its size
+ * Calls that share a workspace must be ordered (one stream, or synchronised): concurrent calls
+ * on one workspace race.
+ * Errors: as bsgemm_grouped, plus BSG_ERR_NULL (workspace NULL), BSG_ERR_ALIGN, BSG_ERR_SHAPE
+ * (workspace too small).
+ */
+int bsgemm_grouped_ws(const void* A, const void* a_scales, const void* B, const void* b_scales,
+                      const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles,
+                      void* C, int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * bsgemm_route_counts - picks per expert: the row counts of the grouped A.

@@ -108,11 +108,15 @@ extern "C" int bsgemm_quantize_permute(const void* x, uint32_t x_dtype, const in
   return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
 }
 
-extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B,
-                              const void* b_scales, const int32_t* expert_ids,
-                              const int32_t* tile_offsets, int32_t num_tiles, void* C, int32_t M,
-                              int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
-                              void* stream) {
+namespace {
+
+// Validation and argument set-up shared by the bsgemm_grouped entry points. Returns BSG_OK with
+// *noop set when there is nothing to launch.
+int grouped_args(const void* A, const void* a_scales, const void* B, const void* b_scales,
+                 const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles, void* C,
+                 int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt, bsg::GemmArgs* args,
+                 bool* noop) {
+  *noop = false;
   const unsigned fa = fmt & 0xF, fb = (fmt >> 4) & 0xF, sk = (fmt >> 8) & 0xF, out = (fmt >> 12) & 0xF;
   const unsigned hint = fmt >> 16;
   if (hint > 1 || out < BSG_OUT_F32 || out > BSG_OUT_F16) return BSG_ERR_FMT;
@@ -137,32 +141,87 @@ extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scales, scale_align) ||
       !aligned(b_scales, scale_align) || (!dense && (!aligned(expert_ids, 4) || !aligned(tile_offsets, 4))))
     return BSG_ERR_ALIGN;
-  if (M == 0 || (!dense && num_tiles == 0)) return BSG_OK;
+  if (M == 0 || (!dense && num_tiles == 0)) {
+    *noop = true;
+    return BSG_OK;
+  }
   int num_cus = 0;
   if (int st = check_device(&num_cus)) return st;
 
-  bsg::GemmArgs args;
-  args.A = A;
-  args.a_scales = a_scales;
-  args.B = B;
-  args.b_scales = b_scales;
-  args.expert_ids = dense ? nullptr : expert_ids;
-  args.tile_offsets = dense ? nullptr : tile_offsets;
-  args.C = C;
-  args.M = M;
-  args.N = N;
-  args.K = K;
-  args.num_experts = dense ? 1 : num_experts;
-  args.num_tiles = dense ? (M + 127) / 128 : num_tiles;
-  args.num_cus = num_cus;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  args->A = A;
+  args->a_scales = a_scales;
+  args->B = B;
+  args->b_scales = b_scales;
+  args->expert_ids = dense ? nullptr : expert_ids;
+  args->tile_offsets = dense ? nullptr : tile_offsets;
+  args->C = C;
+  args->M = M;
+  args->N = N;
+  args->K = K;
+  args->num_experts = dense ? 1 : num_experts;
+  args->num_tiles = dense ? (M + 127) / 128 : num_tiles;
+  args->num_cus = num_cus;
+  return BSG_OK;
+}
+
+// The launch for a validated call: blockwise with the split schedule when a workspace is given.
+int grouped_launch(const bsg::GemmArgs& args, uint32_t fmt, void* workspace, size_t workspace_bytes,
+                   hipStream_t s) {
+  const unsigned fa = fmt & 0xF, fb = (fmt >> 4) & 0xF, sk = (fmt >> 8) & 0xF, out = (fmt >> 12) & 0xF;
+  const unsigned hint = fmt >> 16;
   hipError_t err;
-  if (sk == BSG_SCALE_BLOCKWISE)
-    err = hint ? bsg::launch_blockwise_fp8_small_m(args, static_cast<int>(out), s)
-               : bsg::launch_blockwise_fp8(args, static_cast<int>(out), s);
-  else if (sk == BSG_SCALE_MX)
+  if (sk == BSG_SCALE_BLOCKWISE) {
+    if (hint)
+      err = bsg::launch_blockwise_fp8_small_m(args, static_cast<int>(out), s);
+    else if (workspace)
+      err = bsg::launch_blockwise_fp8_split(args, static_cast<int>(out), workspace, workspace_bytes, s);
+    else
+      err = bsg::launch_blockwise_fp8(args, static_cast<int>(out), s);
+  } else if (sk == BSG_SCALE_MX) {
     err = bsg::launch_mx(args, static_cast<int>(fa), static_cast<int>(fb), static_cast<int>(out), s);
-  else
+  } else {
     err = bsg::launch_nvfp4(args, static_cast<int>(out), s);
+  }
   return err == hipSuccess ? BSG_OK : BSG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int bsgemm_grouped(const void* A, const void* a_scales, const void* B,
+                              const void* b_scales, const int32_t* expert_ids,
+                              const int32_t* tile_offsets, int32_t num_tiles, void* C, int32_t M,
+                              int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                              void* stream) {
+  bsg::GemmArgs args;
+  bool noop;
+  if (int st = grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, num_tiles, C, M, N, K,
+                            num_experts, fmt, &args, &noop))
+    return st;
+  if (noop) return BSG_OK;
+  return grouped_launch(args, fmt, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int bsgemm_grouped_workspace_size(size_t* bytes) {
+  if (!bytes) return BSG_ERR_NULL;
+  int num_cus = 0;
+  if (int st = check_device(&num_cus)) return st;
+  *bytes = bsg::blockwise_fp8_workspace_bytes(num_cus);
+  return BSG_OK;
+}
+
+extern "C" int bsgemm_grouped_ws(const void* A, const void* a_scales, const void* B,
+                                 const void* b_scales, const int32_t* expert_ids,
+                                 const int32_t* tile_offsets, int32_t num_tiles, void* C, int32_t M,
+                                 int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  bsg::GemmArgs args;
+  bool noop;
+  if (int st = grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, num_tiles, C, M, N, K,
+                            num_experts, fmt, &args, &noop))
+    return st;
+  if (!workspace) return BSG_ERR_NULL;
+  if (!aligned(workspace, 256)) return BSG_ERR_ALIGN;
+  if (noop) return BSG_OK;
+  if (workspace_bytes < bsg::blockwise_fp8_workspace_bytes(args.num_cus)) return BSG_ERR_SHAPE;
+  return grouped_launch(args, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }

@@ -65,6 +65,16 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
 // touch 16 different 16-byte bank groups.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Column (within its 128-column block) held by LDS row l of a 128-row B tile half. Fragment j of a
+// wave reads LDS rows 16 j .. 16 j + 15, and its MFMA gives lane (r16, q) the outputs of LDS rows
+// 16 j + 4 q .. 16 j + 4 q + 3. Mapping row 16 j + 4 q + i to column 32 (j / 2) + 8 q + 4 (j % 2) + i
+// gives the lane 8 consecutive columns in fragments 2 jj and 2 jj + 1: one 16-byte store of a
+// bf16 / fp16 result, and the 4 lanes of a row cover 64 consecutive bytes.
+__device__ __forceinline__ int b_col(int l) {
+  const int j = l >> 4, q = (l >> 2) & 3, i = l & 3;
+  return ((j >> 1) << 5) | (q << 3) | ((j & 1) << 2) | i;
+}
+
 // Output conversions (round to nearest even). A pair of fp32 values becomes one dword of two
 // bf16 (gfx950 converts a pair in one instruction, v_cvt_pk_bf16_f32) or two fp16.
 typedef float v2f_t __attribute__((ext_vector_type(2)));

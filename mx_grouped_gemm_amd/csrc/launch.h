@@ -18,10 +18,19 @@ struct GemmArgs {
   int num_experts;
   int num_tiles;  // M-tiles of 128 rows to visit
   int num_cus;    // compute units of the device (size of a persistent grid)
+  int group_m;    // blockwise work order: super-tiles per group (set by the launcher)
 };
 
 // Blockwise-FP8 (e4m3 x e4m3, fp32 1x128 / 128x128 scales). out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream);
+
+// Blockwise-FP8 with a workspace: when the grid's last round of work items would be partly idle,
+// the last one to two rounds are split along K over all workgroups (fp32 partial tiles and flags
+// in ws; a cooperative launch). Falls back to launch_blockwise_fp8 when that does not pay.
+hipError_t launch_blockwise_fp8_split(const GemmArgs& a, int out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Workspace bytes launch_blockwise_fp8_split needs on a device of num_cus compute units.
+size_t blockwise_fp8_workspace_bytes(int num_cus);
 
 // Blockwise-FP8 scheduled for M-tiles of few rows: one work item per M-tile x 256 columns.
 hipError_t launch_blockwise_fp8_small_m(const GemmArgs& a, int out, hipStream_t stream);

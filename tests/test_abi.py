@@ -107,3 +107,14 @@ def test_nvfp4_validation():
     assert grouped(fmt=nv, sa=P4) == -3
     assert grouped(fmt=nv, sb=P4) == -3
     assert grouped(fmt=nv, M=0) == 0
+
+
+def test_grouped_ws_validation():
+    """Workspace checks that come before any device use (M = 0 is a no-op otherwise)."""
+    lib = bsg.load_library()
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
+    args = (P16, P16, P16, P16, None, None, 0, P16, 0, 256, 512, 1, fmt)
+    assert lib.bsgemm_grouped_ws(*args, None, 1 << 30, None) == -1      # workspace NULL
+    assert lib.bsgemm_grouped_ws(*args, P16 + 16, 1 << 30, None) == -3  # not 256-byte aligned
+    assert lib.bsgemm_grouped_ws(*args, P16, 1 << 30, None) == 0        # M = 0: nothing to do
+    assert lib.bsgemm_grouped_workspace_size(None) == -1

@@ -300,6 +300,9 @@ WORKLOADS = {
     # one dense group 4096^3, every 64th row of A and of B scaled x100, bf16 output
     "dense_4096": lambda dev, seed: _blockwise_problem(
         "dense_4096", None, 4096, 4096, 1, ("bf16",), dev, seed, outlier_every=64, a_rows=4096),
+    # one dense group with few 256 x 256 tiles and a long K (8 tiles, K = 16384), bf16 output
+    "dense_256x2048x16384": lambda dev, seed: _blockwise_problem(
+        "dense_256x2048x16384", None, 2048, 16384, 1, ("bf16",), dev, seed, a_rows=256),
     # 8 experts, 4096 tokens top-2, Dirichlet(0.5), N=2048, K=4096, bf16
     "moe8_n2048_k4096": lambda dev, seed: _blockwise_problem(
         "moe8_n2048_k4096", routing_counts(seed=seed, **MOE8), 2048, 4096, 8, ("bf16",), dev, seed),
