@@ -97,8 +97,9 @@ template <int FA, int FB, int KS>
 struct MxLoadPlan {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
   uint32_t a_voff[Layout<FA, FB, KS>::A_INSTR], b_voff[Layout<FA, FB, KS>::B_INSTR];
-  uint32_t sc_voff_a, sc_voff_b;   // scale chunk: lane part (row and dword inside the chunk)
-  uint32_t sc_row8_a, sc_row8_b;   // scale chunk: bytes of 8 rows of the scale tensors
+  uint32_t sc_voff_a;              // A scale chunk: lane part (row and dword inside the chunk)
+  uint32_t sc_row8_a;              // A scale chunk: bytes of 8 rows of the scale tensor
+  uint32_t sc_voff_b[SC_INSTR];    // B scale chunk: per copy (B rows are permuted, see b_col)
   int a_dst, b_dst;
 };
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ void mx_issue_scales(uint8_t* __restrict__ dsa, uint8
 #pragma unroll
   for (int i = 0; i < SC_INSTR; i++) {
     buf2lds4(lp.sa_rsrc, lp.sc_voff_a + col + i * lp.sc_row8_a, 0, as_lds(dsa + (wave * SC_INSTR + i) * 256));
-    buf2lds4(lp.sb_rsrc, lp.sc_voff_b + col + i * lp.sc_row8_b, 0, as_lds(dsb + (wave * SC_INSTR + i) * 256));
+    buf2lds4(lp.sb_rsrc, lp.sc_voff_b[i] + col, 0, as_lds(dsb + (wave * SC_INSTR + i) * 256));
   }
 }
 
@@ -205,17 +206,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         const int r = (wave * L::A_INSTR + i) * PA + lane / CA, slot = lane % CA;
         lp.a_voff[i] = (uint32_t)(r * rowA + ((slot ^ swzr<L::RA>(r)) * 16));
       }
+      // LDS row r of the B half holds B row (r & 128) | b_col(r & 127) (and so do the B scales),
+      // so that the epilogue stores 16 bytes per lane; the swizzle follows the LDS row
 #pragma unroll
       for (int i = 0; i < L::B_INSTR; i++) {
         const int r = (wave * L::B_INSTR + i) * PB + lane / CB, slot = lane % CB;
-        lp.b_voff[i] = (uint32_t)(r * rowB + ((slot ^ swzr<L::RB>(r)) * 16));
+        lp.b_voff[i] = (uint32_t)(((r & 128) | b_col(r & 127)) * rowB + ((slot ^ swzr<L::RB>(r)) * 16));
       }
       lp.a_dst = wave * L::A_INSTR * 1024;
       lp.b_dst = wave * L::B_INSTR * 1024;
       const int lrow = lane >> 3, dw = lane & 7;                 // scale chunk: 8 rows x 8 dwords
       lp.sc_voff_a = (uint32_t)((wave * 32 + lrow) * srow + dw * 4);
-      lp.sc_voff_b = lp.sc_voff_a;
-      lp.sc_row8_a = lp.sc_row8_b = (uint32_t)(8 * srow);
+      lp.sc_row8_a = (uint32_t)(8 * srow);
+#pragma unroll
+      for (int i = 0; i < SC_INSTR; i++) {
+        const int r = wave * 32 + 8 * i + lrow;
+        lp.sc_voff_b[i] = (uint32_t)(((r & 128) | b_col(r & 127)) * srow + dw * 4);
+      }
     }
 
     v4f acc[MI][NJ];
@@ -379,16 +386,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
     }
     wait_vmcnt<0>();
 
-    // epilogue: lane holds row r16 of each M fragment and columns 4 q .. 4 q + 3 of each N fragment
+    // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
+    // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col)
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       const int mloc = wm * WM + i * 16 + r16;
       if (mloc >= rows) continue;
       const size_t crow = (size_t)(row0 + mloc) * N;
 #pragma unroll
-      for (int j = 0; j < NJ; j++) {
-        const int col = n0 + wn * WN + j * 16 + q * 4;
-        if (col < N) store4<OUT>(p.C, crow + col, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int jj = 0; jj < NJ / 2; jj++) {
+        const int col = n0 + wn * WN + jj * 32 + q * 8;
+        if (col < N) store8<OUT>(p.C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
       }
     }
     if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass
