@@ -188,6 +188,26 @@ int bsgemm_grouped_ws(const void* A, const void* a_scales, const void* B, const 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bsgemm_grouped_noalloc - bsgemm_grouped_ws without a workspace argument, allocating nothing.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same operation, arguments, results and errors as
+ * bsgemm_grouped; its split-K schedule for small problems (see bsgemm_grouped_ws) uses a scratch
+ * array the library holds on each device it runs on, for the life of the process: 16 MiB + 4 KiB,
+ * room for 64 partial tiles. Where bsgemm_grouped_ws would cut the items into more ranges than
+ * 64 tiles, fewer ranges are used, so no call needs more scratch than the array holds and none
+ * is rejected for it (results are within the same tolerance). The scratch's flags are cleared on
+ * the stream at the start of every split launch.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU (different streams
+ * or host threads without ordering) race and give wrong results. No hipMalloc, hipFree or other
+ * allocating call is made.
+ */
+int bsgemm_grouped_noalloc(const void* A, const void* a_scales, const void* B, const void* b_scales,
+                           const int32_t* expert_ids, const int32_t* tile_offsets, int32_t num_tiles,
+                           void* C, int32_t M, int32_t N, int32_t K, int32_t num_experts, uint32_t fmt,
+                           void* stream);
+
+/*
  * bsgemm_route_counts - picks per expert: the row counts of the grouped A.
  *
  * Passage: "promote_accumulators", section Args, argument expert_ids (each group of A's rows

@@ -14,6 +14,7 @@ import torch
 __all__ = [
     "BsgemmError", "ELEM", "SCALE", "OUT", "make_fmt", "bsgemm_build_tiles", "bsgemm_grouped",
     "check_grouped_args", "check_permute_args", "bsgemm_grouped_workspace_size", "bsgemm_grouped_ws",
+    "bsgemm_grouped_noalloc",
     "bsgemm_status_string", "bsgemm_route_counts", "bsgemm_quantize_permute", "library_path",
     "load_library",
 ]
@@ -27,7 +28,8 @@ SCALE = {"blockwise": 1, "mx": 2, "nv": 3}
 OUT = {"f32": 1, "bf16": 2, "f16": 3}
 OUT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 EXPORTED = ("bsgemm_build_tiles", "bsgemm_grouped", "bsgemm_status_string", "bsgemm_route_counts",
-            "bsgemm_quantize_permute", "bsgemm_grouped_workspace_size", "bsgemm_grouped_ws")
+            "bsgemm_quantize_permute", "bsgemm_grouped_workspace_size", "bsgemm_grouped_ws",
+            "bsgemm_grouped_noalloc")
 
 
 class BsgemmError(RuntimeError):
@@ -64,6 +66,8 @@ def load_library():
     lib.bsgemm_grouped_ws.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, u32, vp,
                                       ctypes.c_size_t, vp]
     lib.bsgemm_grouped_ws.restype = ctypes.c_int
+    lib.bsgemm_grouped_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, u32, vp]
+    lib.bsgemm_grouped_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -245,6 +249,28 @@ def bsgemm_grouped_ws(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, 
         _nbytes(workspace), _stream(stream))
     if st != 0:
         raise BsgemmError("bsgemm_grouped_ws", st)
+    return C
+
+
+def bsgemm_grouped_noalloc(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, M, N, K, fmt,
+                           num_tiles=None, num_experts=None, stream=None):
+    """``bsgemm_grouped_ws`` with the library's own device scratch instead of a workspace: for
+    callers that cannot allocate. Concurrent calls on one GPU race on that scratch."""
+    for t, n in ((A, "A"), (a_scales, "a_scales"), (B, "B"), (b_scales, "b_scales"), (C, "C")):
+        _dev(t, n)
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(tile_offsets, "tile_offsets", torch.int32)
+    if num_tiles is None:
+        num_tiles = expert_ids.numel() if expert_ids is not None else 0
+    if num_experts is None:
+        num_experts = B.shape[0] if B.dim() == 3 else 1
+    check_grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, C, int(M), int(N), int(K),
+                       int(fmt), int(num_tiles), int(num_experts))
+    st = load_library().bsgemm_grouped_noalloc(
+        _ptr(A), _ptr(a_scales), _ptr(B), _ptr(b_scales), _ptr(expert_ids), _ptr(tile_offsets),
+        int(num_tiles), _ptr(C), int(M), int(N), int(K), int(num_experts), int(fmt), _stream(stream))
+    if st != 0:
+        raise BsgemmError("bsgemm_grouped_noalloc", st)
     return C
 
 

@@ -40,6 +40,7 @@
 //    loop without reads, MFMAs or promotion, keeping only their copies, waits and barriers: a
 //    lone 128-row tile then costs its SIMDs one wave's matrix work instead of two (the 8-expert
 //    configuration, 8 such passes in 38, ran 12 % faster).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -737,11 +738,14 @@ hipError_t launch_blockwise_fp8_split(const GemmArgs& a, int out, void* ws, size
   // items the split is not used: cutting only the last round's items measured no faster than
   // running them whole (the partial tiles' traffic and the second launch cost what the idle
   // workgroups lose).
+  // A workspace smaller than blockwise_fp8_workspace_bytes (at least the flags) holds fewer
+  // partial tiles; the split then uses fewer ranges, so that every range has its tile.
+  if (ws == nullptr || ws_bytes < SPLIT_FLAG_BYTES) return hipErrorInvalidValue;
+  const long long slots = std::min<long long>(G, (long long)((ws_bytes - SPLIT_FLAG_BYTES) / SPLIT_SLOT_BYTES));
   const long long tail = items < (long long)G ? items : 0;
   int parts = 1;
-  while (tail > 0 && parts < 16 && 2 * parts * 8 <= KB && tail * 2 * parts <= (long long)G) parts *= 2;
+  while (tail > 0 && parts < 16 && 2 * parts * 8 <= KB && tail * 2 * parts <= slots) parts *= 2;
   if (parts < 2 || G > SPLIT_FLAG_BYTES / 4 - 1) return launch_blockwise_fp8(a, out, stream);
-  if (ws == nullptr || ws_bytes < blockwise_fp8_workspace_bytes(a.num_cus)) return hipErrorInvalidValue;
   const int words = (int)(SPLIT_FLAG_BYTES / 4);
   hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream, (int*)ws, words);
   hipError_t err = hipGetLastError();

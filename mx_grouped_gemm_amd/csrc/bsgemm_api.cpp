@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -42,6 +43,31 @@ int check_device(int* num_cus = nullptr) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Scratch of bsgemm_grouped_noalloc: the workspace of the split-K schedule (4 KiB of flags, then
+// 64 fp32 partial tiles of 256 x 256) as a device array the library holds for the process's
+// lifetime on every device it runs on. Host code uses its device address per device, never the
+// array's host-side name.
+constexpr size_t kScratchBytes = 4096 + 64 * (size_t)256 * 256 * 4;   // 16 MiB + 4 KiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of scratch on device dev (the current device), looked up once per device.
+void* scratch_ptr(int dev) {
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 }  // namespace
 
@@ -224,4 +250,25 @@ extern "C" int bsgemm_grouped_ws(const void* A, const void* a_scales, const void
   if (noop) return BSG_OK;
   if (workspace_bytes < bsg::blockwise_fp8_workspace_bytes(args.num_cus)) return BSG_ERR_SHAPE;
   return grouped_launch(args, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int bsgemm_grouped_noalloc(const void* A, const void* a_scales, const void* B,
+                                      const void* b_scales, const int32_t* expert_ids,
+                                      const int32_t* tile_offsets, int32_t num_tiles, void* C,
+                                      int32_t M, int32_t N, int32_t K, int32_t num_experts,
+                                      uint32_t fmt, void* stream) {
+  bsg::GemmArgs args;
+  bool noop;
+  if (int st = grouped_args(A, a_scales, B, b_scales, expert_ids, tile_offsets, num_tiles, C, M, N, K,
+                            num_experts, fmt, &args, &noop))
+    return st;
+  if (noop) return BSG_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return BSG_ERR_DEVICE;
+  }
+  void* ws = scratch_ptr(dev);
+  if (!ws) return BSG_ERR_DEVICE;
+  return grouped_launch(args, fmt, ws, kScratchBytes, static_cast<hipStream_t>(stream));
 }

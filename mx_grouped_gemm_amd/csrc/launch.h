@@ -24,9 +24,9 @@ struct GemmArgs {
 // Blockwise-FP8 (e4m3 x e4m3, fp32 1x128 / 128x128 scales). out: 1 f32, 2 bf16, 3 f16.
 hipError_t launch_blockwise_fp8(const GemmArgs& a, int out, hipStream_t stream);
 
-// Blockwise-FP8 with a workspace: when the grid's last round of work items would be partly idle,
-// the last one to two rounds are split along K over all workgroups (fp32 partial tiles and flags
-// in ws; a cooperative launch). Falls back to launch_blockwise_fp8 when that does not pay.
+// Blockwise-FP8 with a workspace: with fewer work items than compute units each item is cut along
+// K into ranges that run side by side (fp32 partial tiles and flags in ws; at most as many
+// ranges as ws holds tiles). Falls back to launch_blockwise_fp8 when that does not apply.
 hipError_t launch_blockwise_fp8_split(const GemmArgs& a, int out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Workspace bytes launch_blockwise_fp8_split needs on a device of num_cus compute units.
