@@ -61,7 +61,7 @@ METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 # HBM bytes per gate_up launch: rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
 # 1 GiB device copy measured with the same counters). Valid only for the kernel source whose
 # sha256 starts with this prefix; reported as null for any other source.
-GATE_UP_TRAFFIC = ("d06aaba582cfd4ea", 14.90e9)
+GATE_UP_TRAFFIC = ("f22ccf302c696378", 11.94e9)
 KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
 
 
@@ -119,7 +119,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(problems, n_experts=1):
+def cpu_baseline(problems, n_experts=8):
     """Time the oracle on a bounded sample of the step: every real row of the first ``n_experts``
     non-empty experts, for both GEMMs (gate_up and down). The oracle is the product by its
     definition (``blockwise_grouped_dequant``: decode and scale into fp64, then one BLAS product
