@@ -6,8 +6,9 @@
 //
 // CDNA4 mapping: v_mfma_scale_f32_16x16x128_f8f6f4 takes one e8m0 scale per lane, so the scales
 // are applied by the matrix unit, the fp32 accumulator chains through the instruction and no
-// software promotion is needed. Block structure as in the blockwise kernel: 256 x 256 block
-// tiles (super-tiles of two 128-row M-tiles of one expert), 8 waves of 64 x 128 as 4 x 8
+// software promotion is needed. Block structure as in the blockwise kernel: a persistent grid
+// (one workgroup per compute unit) over 256 x 256 work items (super-tiles of two 128-row M-tiles
+// of one expert) with one copy pipeline across a workgroup's items, 8 waves of 64 x 128 as 4 x 8
 // fragments of 16 x 16, A fragments resident and B fragments streamed two ahead, a 2-stage LDS
 // ring filled by buffer -> LDS copies, one barrier per K block. The scales of a super-tile's
 // rows are staged 8 K blocks at a time (one dword of four scales per row and K block).
@@ -16,15 +17,18 @@
 // supplied by lane 16 c + r, so lane (r16 = l % 16, q = l / 16) supplies chunk q of its row.
 // e2m1: lane (r16, q) holds chunk q itself (16 bytes, low nibble = even K). e4m3: lane (r16, q)
 // holds K [16 q, 16 q + 16) in bytes 0..15 and K [64 + 16 q, 64 + 16 q + 16) in bytes 16..31.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace bsg {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 128, TILE_M = 128;
+constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int NWAVES = 8, NTHREADS = NWAVES * kWave;
 constexpr int WM = 64, WN = 128;                  // wave tile
 constexpr int MI = WM / 16, NJ = WN / 16;         // 4 x 8 fragments of 16 x 16
@@ -44,9 +48,9 @@ template <int FA, int FB, int KS>
 struct Layout {
   static constexpr int RA = Elem<FA>::kRowBytes * KS, RB = Elem<FB>::kRowBytes * KS;
   static constexpr int A_BYTES = BM * RA, B_BYTES = BN * RB;       // per stage
-  static constexpr int A_REGION = 0;
-  static constexpr int B_REGION = STAGES * A_BYTES;
-  static constexpr int SA_REGION = B_REGION + STAGES * B_BYTES;    // 2 chunks of A scales
+  static constexpr int B_REGION = 0;
+  static constexpr int A_REGION = STAGES * B_BYTES;
+  static constexpr int SA_REGION = A_REGION + STAGES * A_BYTES;    // 2 chunks of A scales
   static constexpr int SB_REGION = SA_REGION + 2 * SC_BYTES;       // 2 chunks of B scales
   static constexpr int LDS_BYTES = SB_REGION + 2 * SC_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;          // 1 KiB copies per wave
@@ -97,36 +101,63 @@ template <int FA, int FB, int KS>
 struct MxLoadPlan {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
   uint32_t a_voff[Layout<FA, FB, KS>::A_INSTR], b_voff[Layout<FA, FB, KS>::B_INSTR];
-  uint32_t sc_voff_a;              // A scale chunk: lane part (row and dword inside the chunk)
-  uint32_t sc_row8_a;              // A scale chunk: bytes of 8 rows of the scale tensor
-  uint32_t sc_voff_b[SC_INSTR];    // B scale chunk: per copy (B rows are permuted, see b_col)
-  int a_dst, b_dst;
+  uint32_t srow;                   // bytes of one row of the scale tensors
 };
 
-// Copy i (of A_INSTR / B_INSTR per wave) of K block kb into the A or B half of a stage.
+// LDS destinations are 32-bit LDS addresses: this wave's bases (see lds_bases) plus constants.
+__device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(size_t)a; }
+
+// This wave's copy destination bases: wa / wb for its part of an A / B tile, ws for its rows of a
+// scale chunk. Re-derived through an empty asm at every stage so that the compiler forms each
+// destination (base + constant) next to its copy instead of keeping every combination live in
+// SGPRs.
+struct LdsBases {
+  uint32_t wa, wb, ws;
+};
 template <int FA, int FB, int KS>
-__device__ __forceinline__ void mx_copy_a(uint8_t* __restrict__ da, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
+__device__ __forceinline__ LdsBases lds_bases(const uint8_t* smem, int wave) {
   using L = Layout<FA, FB, KS>;
-  buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RA,
-            as_lds(da + lp.a_dst + i * 1024));
+  const uint32_t s0 = (uint32_t)(size_t)as_lds(const_cast<uint8_t*>(smem));
+  LdsBases l;
+  l.wa = s0 + wave * L::A_INSTR * 1024;
+  l.wb = s0 + wave * L::B_INSTR * 1024;
+  l.ws = s0 + wave * SC_INSTR * 256;
+  asm volatile("" : "+s"(l.wa), "+s"(l.wb), "+s"(l.ws));
+  return l;
+}
+
+// Copy i (of A_INSTR / B_INSTR per wave) of K block kb to LDS address dst (the stage's A or B
+// tile plus this wave's part).
+template <int FA, int FB, int KS>
+__device__ __forceinline__ void mx_copy_a(uint32_t dst, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
+  using L = Layout<FA, FB, KS>;
+  buf2lds16(lp.a_rsrc, lp.a_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RA, lds_ptr(dst + i * 1024));
 }
 template <int FA, int FB, int KS>
-__device__ __forceinline__ void mx_copy_b(uint8_t* __restrict__ db, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
+__device__ __forceinline__ void mx_copy_b(uint32_t dst, const MxLoadPlan<FA, FB, KS>& lp, int kb, int i) {
   using L = Layout<FA, FB, KS>;
-  buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RB,
-            as_lds(db + lp.b_dst + i * 1024));
+  buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RB, lds_ptr(dst + i * 1024));
 }
 
 // Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows into
-// [row][8 dwords] layouts; wave w copies rows 32 w .. 32 w + 31 of each.
+// [row][8 dwords] layouts; wave w copies rows 32 w .. 32 w + 31 of each (instruction i: rows
+// 32 w + 8 i + lane / 8, dword lane % 8; LDS row r of the B half holds B row (r & 128) |
+// b_col(r & 127), as the B tile does). The per-lane offsets are formed here, once per chunk (an
+// empty asm keeps the compiler from keeping them live across the K loop).
 template <int FA, int FB, int KS>
-__device__ __forceinline__ void mx_issue_scales(uint8_t* __restrict__ dsa, uint8_t* __restrict__ dsb,
-                                                const MxLoadPlan<FA, FB, KS>& lp, int chunk, int wave) {
+__device__ __forceinline__ void mx_issue_scales(uint32_t dsa, uint32_t dsb, const MxLoadPlan<FA, FB, KS>& lp,
+                                                int chunk, int wave) {
   const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * SC_CHUNK * 4;
+  int ln = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(ln));
+  const int lrow = ln >> 3, dw = ln & 7;
 #pragma unroll
   for (int i = 0; i < SC_INSTR; i++) {
-    buf2lds4(lp.sa_rsrc, lp.sc_voff_a + col + i * lp.sc_row8_a, 0, as_lds(dsa + (wave * SC_INSTR + i) * 256));
-    buf2lds4(lp.sb_rsrc, lp.sc_voff_b[i] + col, 0, as_lds(dsb + (wave * SC_INSTR + i) * 256));
+    const int r = wave * 32 + 8 * i + lrow;
+    const uint32_t va = (uint32_t)r * lp.srow + dw * 4 + col;
+    const uint32_t vb = (uint32_t)((r & 128) | b_col(r & 127)) * lp.srow + dw * 4 + col;
+    buf2lds4(lp.sa_rsrc, va, 0, lds_ptr(dsa + i * 256));
+    buf2lds4(lp.sb_rsrc, vb, 0, lds_ptr(dsb + i * 256));
   }
 }
 
@@ -146,116 +177,121 @@ __device__ __forceinline__ v8i sub_op(const v8i& x, int h) {
 }
 
 template <int FA, int FB, int OUT, int KS>
-__global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_blocks) {
+__global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_blocks,
+                                                        const int32_t* __restrict__ expert_ids,
+                                                        const int32_t* __restrict__ tile_offsets,
+                                                        void* __restrict__ C) {
   using L = Layout<FA, FB, KS>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::LDS_BYTES];
+  const TileMap tm = {expert_ids, tile_offsets};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int num_super = (p.num_tiles + 1) / 2;
-  int s, nb;
-  if (!work_item(num_super, n_blocks, 8, s, nb)) return;
-  const int n0 = nb * BN, N = p.N, KB = p.K / (BK * KS);          // stages
+  const int items = ((p.num_tiles + 1) / 2) * n_blocks;
+  const int N = p.N, KB = p.K / (BK * KS);                         // stages per unit
   const size_t rowA = (size_t)p.K * Elem<FA>::kRowBytes / BK;      // bytes per row
   const size_t rowB = (size_t)p.K * Elem<FB>::kRowBytes / BK;
   constexpr int SCS = SC_CHUNK / KS;                                // stages per scale chunk
-  const size_t srow = (size_t)p.K / 32;                                            // scale bytes per row
+  const int nchunks = (KB + SCS - 1) / SCS;                        // scale chunks per unit
+  const size_t srow = (size_t)p.K / 32;                            // scale bytes per row
   const int wm = wave >> 1, wn = wave & 1;                  // rows 64 wm, cols 128 wn
   const int r16 = lane & 15, q = lane >> 4;
-  const int ncols = min(BN, N - n0);
-
-  // the super-tile's passes, as in the blockwise kernel
-  const TileRows t0 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s, p.M, TILE_M, p.num_experts);
-  TileRows t1 = {0, 0, 0};
-  if (2 * s + 1 < p.num_tiles)
-    t1 = tile_rows(p.expert_ids, p.tile_offsets, 2 * s + 1, p.M, TILE_M, p.num_experts);
-  int e0 = t0.expert, r0 = t0.row0, n0rows = t0.rows, e1 = t1.expert, r1 = t1.row0, n1rows = t1.rows;
-  int npass;
-  if (t0.rows == TILE_M && t1.rows > 0 && t1.expert == t0.expert && t1.row0 == t0.row0 + TILE_M) {
-    n0rows = TILE_M + t1.rows;
-    npass = 1;
-  } else if (t0.rows > 0) {
-    npass = t1.rows > 0 ? 2 : 1;
-  } else {
-    e0 = e1; r0 = r1; n0rows = n1rows;
-    npass = t1.rows > 0 ? 1 : 0;
-  }
+  // Consecutive stages of the units of this workgroup share one pipeline, as in the blockwise
+  // kernel: the last two stages of a unit copy the first two of the next (and its first two scale
+  // chunks), so only the first unit has a prologue and a unit's stores drain under the next one's
+  // first passes. This needs an even number of stages per unit; with an odd number every unit
+  // starts with its own prologue.
+  const bool piped = (KB & 1) == 0;
+  // Work order as in the blockwise kernel: the grid is a multiple of 8, block b runs on XCD b % 8,
+  // and the blocks of one XCD take contiguous runs of logical items.
+  const int xb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
 
   const FragBase<L::RA> fa = frag_base<L::RA>(wm * WM + r16, r16, q);
   const FragBase<L::RB> fb = frag_base<L::RB>(wn * WN + r16, r16, q);
   const int base_sa = L::SA_REGION + (wm * WM + r16) * SC_CHUNK * 4;
   const int base_sb = L::SB_REGION + (wn * WN + r16) * SC_CHUNK * 4;
 
-  for (int ps = 0; ps < npass; ps++) {
-    const int e = __builtin_amdgcn_readfirstlane(ps == 0 ? e0 : e1);
-    const int row0 = __builtin_amdgcn_readfirstlane(ps == 0 ? r0 : r1);
-    const int rows = __builtin_amdgcn_readfirstlane(ps == 0 ? n0rows : n1rows);
-
-    // Copy plan. Every row offset is in the per-lane offset, which the resource bounds check:
-    // rows past the pass or past N read as zero.
-    MxLoadPlan<FA, FB, KS> lp;
-    lp.a_rsrc = make_rsrc((const uint8_t*)p.A + (size_t)row0 * rowA, (uint64_t)rows * rowA);
-    lp.b_rsrc = make_rsrc((const uint8_t*)p.B + ((size_t)e * N + n0) * rowB, (uint64_t)ncols * rowB);
-    lp.sa_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)row0 * srow, (uint64_t)rows * srow);
-    lp.sb_rsrc = make_rsrc((const uint8_t*)p.b_scales + ((size_t)e * N + n0) * srow, (uint64_t)ncols * srow);
-    {
-      constexpr int CA = L::RA / 16, CB = L::RB / 16;            // 16-byte chunks per tile row
-      constexpr int PA = 1024 / L::RA, PB = 1024 / L::RB;        // tile rows per 1 KiB copy
+  // Copy plan. The per-lane offsets depend only on the lane, the wave and K; the resources
+  // describe the unit being copied (rows past it or past N read as zero) and switch from one unit
+  // to the next at the first stage whose copies target the next one.
+  MxLoadPlan<FA, FB, KS> lp;
+  {
+    constexpr int CA = L::RA / 16, CB = L::RB / 16;            // 16-byte chunks per tile row
+    constexpr int PA = 1024 / L::RA, PB = 1024 / L::RB;        // tile rows per 1 KiB copy
 #pragma unroll
-      for (int i = 0; i < L::A_INSTR; i++) {
-        const int r = (wave * L::A_INSTR + i) * PA + lane / CA, slot = lane % CA;
-        lp.a_voff[i] = (uint32_t)(r * rowA + ((slot ^ swzr<L::RA>(r)) * 16));
-      }
-      // LDS row r of the B half holds B row (r & 128) | b_col(r & 127) (and so do the B scales),
-      // so that the epilogue stores 16 bytes per lane; the swizzle follows the LDS row
-#pragma unroll
-      for (int i = 0; i < L::B_INSTR; i++) {
-        const int r = (wave * L::B_INSTR + i) * PB + lane / CB, slot = lane % CB;
-        lp.b_voff[i] = (uint32_t)(((r & 128) | b_col(r & 127)) * rowB + ((slot ^ swzr<L::RB>(r)) * 16));
-      }
-      lp.a_dst = wave * L::A_INSTR * 1024;
-      lp.b_dst = wave * L::B_INSTR * 1024;
-      const int lrow = lane >> 3, dw = lane & 7;                 // scale chunk: 8 rows x 8 dwords
-      lp.sc_voff_a = (uint32_t)((wave * 32 + lrow) * srow + dw * 4);
-      lp.sc_row8_a = (uint32_t)(8 * srow);
-#pragma unroll
-      for (int i = 0; i < SC_INSTR; i++) {
-        const int r = wave * 32 + 8 * i + lrow;
-        lp.sc_voff_b[i] = (uint32_t)(((r & 128) | b_col(r & 127)) * srow + dw * 4);
-      }
+    for (int i = 0; i < L::A_INSTR; i++) {
+      const int r = (wave * L::A_INSTR + i) * PA + lane / CA, slot = lane % CA;
+      lp.a_voff[i] = (uint32_t)(r * rowA + ((slot ^ swzr<L::RA>(r)) * 16));
     }
+    // LDS row r of the B half holds B row (r & 128) | b_col(r & 127) (and so do the B scales),
+    // so that the epilogue stores 16 bytes per lane; the swizzle follows the LDS row
+#pragma unroll
+    for (int i = 0; i < L::B_INSTR; i++) {
+      const int r = (wave * L::B_INSTR + i) * PB + lane / CB, slot = lane % CB;
+      lp.b_voff[i] = (uint32_t)(((r & 128) | b_col(r & 127)) * rowB + ((slot ^ swzr<L::RB>(r)) * 16));
+    }
+    lp.srow = (uint32_t)srow;
+  }
+  auto rsrc_a = [&](const Unit& u, bool live) {
+    return make_rsrc((const uint8_t*)p.A + (size_t)u.row0 * rowA, live ? (uint64_t)u.rows * rowA : 0);
+  };
+  auto rsrc_b = [&](const Unit& u, bool live) {
+    return make_rsrc((const uint8_t*)p.B + ((size_t)u.e * N + u.n0) * rowB,
+                     live ? (uint64_t)min(BN, N - u.n0) * rowB : 0);
+  };
+  auto rsrc_scales = [&](const Unit& u, bool live) {
+    lp.sa_rsrc = make_rsrc((const uint8_t*)p.a_scales + (size_t)u.row0 * srow, live ? (uint64_t)u.rows * srow : 0);
+    lp.sb_rsrc = make_rsrc((const uint8_t*)p.b_scales + ((size_t)u.e * N + u.n0) * srow,
+                           live ? (uint64_t)min(BN, N - u.n0) * srow : 0);
+  };
 
-    v4f acc[MI][NJ];
+  // Scale chunk c of the current unit sits in buffer (cbase + c) & 1.
+  int cbase = 0;
+  v4f acc[MI][NJ];
+
+  // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, moved to byte 0
+  // g: 128-K sub-block index of the unit (stage b holds sub-blocks KS b .. KS b + KS - 1)
+  auto scale_a = [&](int g, int i) {
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
+    return (int)(*(const uint32_t*)(smem + base_sa + so + i * 16 * SC_CHUNK * 4) >> (8 * q));
+  };
+  auto scale_b = [&](int g, int j) {
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
+    return (int)(*(const uint32_t*)(smem + base_sb + so + j * 16 * SC_CHUNK * 4) >> (8 * q));
+  };
+
+  // The stages of unit u into acc. prologue: copy the unit's first stages and scale chunks and
+  // wait for them (else the previous unit's last stages copied them). pipe: the last two stages
+  // copy the first two of unit nx (zero-byte resources unless nx_live).
+  auto run_unit = [&](const Unit& u, const bool prologue, const bool pipe, const Unit& nx, const bool nx_live) {
 #pragma unroll
     for (int i = 0; i < MI; i++)
 #pragma unroll
       for (int j = 0; j < NJ; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    // prologue: scale chunks 0 and 1, block 0 and the B half of block 1 (its A half goes out in
-    // passes 0 and 1 of block 0, as in every block); block 0 published
-    mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION, smem + L::SB_REGION, lp, 0, wave);
-    mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION + SC_BYTES, smem + L::SB_REGION + SC_BYTES, lp, 1, wave);
+    if (prologue) {
+      // copies of the previous unit's last stages may still be in flight into stages reused here
+      wait_vmcnt<0>();
+      cbase = 0;
+      lp.a_rsrc = rsrc_a(u, true);
+      lp.b_rsrc = rsrc_b(u, true);
+      rsrc_scales(u, true);
+      // scale chunks 0 and 1, stage 0 and the B half of stage 1 (its A half goes out in passes 0
+      // and 1 of stage 0, as in every stage); stage 0 published
+      const LdsBases lb = lds_bases<FA, FB, KS>(smem, wave);
+      mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION, lb.ws + L::SB_REGION, lp, 0, wave);
+      mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + SC_BYTES, lb.ws + L::SB_REGION + SC_BYTES, lp, 1, wave);
 #pragma unroll
-    for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB, KS>(smem + L::A_REGION, lp, 0, i);
+      for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB, KS>(lb.wa + L::A_REGION, lp, 0, i);
 #pragma unroll
-    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB, KS>(smem + L::B_REGION, lp, 0, i);
+      for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION, lp, 0, i);
 #pragma unroll
-    for (int i = 0; i < L::B_INSTR; i++) mx_copy_b<FA, FB, KS>(smem + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1), i);
-    wait_vmcnt<0>();
-    barrier();
+      for (int i = 0; i < L::B_INSTR; i++)
+        mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION + L::B_BYTES, lp, min(1, KB - 1), i);
+      wait_vmcnt<0>();
+      barrier();
+    }
 
-    // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, moved to byte 0
-    // g: 128-K sub-block index (stage b holds sub-blocks KS b .. KS b + KS - 1)
-    auto scale_a = [&](int g, int i) {
-      const int so = ((g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
-      return (int)(*(const uint32_t*)(smem + base_sa + so + i * 16 * SC_CHUNK * 4) >> (8 * q));
-    };
-    auto scale_b = [&](int g, int j) {
-      const int so = ((g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
-      return (int)(*(const uint32_t*)(smem + base_sb + so + j * 16 * SC_CHUNK * 4) >> (8 * q));
-    };
-
-    // A fragments and scales of the block stay in registers; B fragments and their scales
+    // A fragments and scales of the stage stay in registers; B fragments and their scales
     // stream through 3-deep queues two fragments ahead
     v8i af[MI], bq[3];
     int sa[MI][KS], sbq[3][KS];
@@ -273,22 +309,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       sbq[1][h] = scale_b(h, 1);
     }
 
-    // copies per wave and pass: the A half of a block over passes 0 and 1, the B half over
+    // copies per wave and pass: the A half of a stage over passes 0 and 1, the B half over
     // passes 6 and 7, each after the second or fourth MFMA of the pass
     constexpr int A_PP = L::A_INSTR / 2, B_PP = L::B_INSTR / 2;
     static_assert(A_PP >= 1 && A_PP <= 2 && B_PP >= 1 && B_PP <= 2, "copy schedule");
 
-    for (int b = 0; b < KB; b++) {
+    // One stage (b) in ring place S = b & 1 (a run-time value: a loop body per place, with the
+    // offsets as immediates, needs more registers than the kernel has). Stages of the main loop
+    // (TAIL false) copy from the current unit only; the last two (TAIL true) copy the next unit's
+    // first stages when piped, else repeat stage KB-1 into a stage that is not read again.
+    auto stage = [&](auto tail_tag, const int b) {
       const int S = b & 1;
-      const int soa = S * L::A_BYTES, sob = S * L::B_BYTES;                 // this block's stage
-      const int sna = (S ^ 1) * L::A_BYTES, snb = (S ^ 1) * L::B_BYTES;
+      constexpr bool TAIL = decltype(tail_tag)::value;
+      const int sob = S * L::B_BYTES;                                            // this stage
+      const int sna = (S ^ 1) * L::A_BYTES, snb = (S ^ 1) * L::B_BYTES;         // the other one
       const int bn = min(b + 1, KB - 1);
+      // copy targets: the A half of stage b+1, the B half of stage b+2
+      int kb_a = b + 1, kb_b = min(b + 2, KB - 1);
+      const LdsBases lb = lds_bases<FA, FB, KS>(smem, wave);
+      if constexpr (TAIL) {
+        if (pipe) {
+          kb_b = b + 2 - KB;
+          if (b == KB - 1) {
+            kb_a = 0;
+            lp.a_rsrc = rsrc_a(nx, nx_live);
+          }
+        } else {
+          kb_a = bn;
+        }
+      }
       // passes 0..5: B fragment j against the 4 resident A fragments (with two sub-blocks per
       // stage: sub-block 0 for all four, then sub-block 1, so chained MFMAs are four apart), MFMAs
-      // at raised wave priority; B fragment j + 2 is read in two halves (after the first and third MFMA) and
-      // its scale after the third. Passes 0 and 1 also copy the A half of block b+1 into the
-      // other stage (freed by the barrier of block b-1; its B half went out in passes 6 and 7
-      // of block b-1). Each MFMA with what follows it is a scheduling region of its own.
+      // at raised wave priority; B fragment j + 2 is read in two halves (after the first and third
+      // MFMA) and its scale after the third. Passes 0 and 1 also copy the A half of stage b+1 into
+      // the other stage (freed by the barrier of stage b-1; its B half went out in passes 6 and 7
+      // of stage b-1). Each MFMA with what follows it is a scheduling region of its own.
 #pragma unroll
       for (int j = 0; j < NJ - 2; j++) {
         __builtin_amdgcn_sched_barrier(0);
@@ -305,7 +360,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
             continue;
           }
           if (j < 2 && (i & 1) && (i >> 1) < A_PP)
-            mx_copy_a<FA, FB, KS>(smem + L::A_REGION + sna, lp, bn, j * A_PP + (i >> 1));
+            mx_copy_a<FA, FB, KS>(lb.wa + L::A_REGION + sna, lp, kb_a, j * A_PP + (i >> 1));
           if (j + 2 < NJ && i == 0) lo = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[0]);
           if (j + 2 < NJ && i == 2) {
             if constexpr (L::RB == 128) hi = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[1]);
@@ -329,20 +384,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // stage S fully read (its last read was in pass 5), block b+1 landed: publish it
+      // stage S fully read (its last read was in pass 5), stage b+1 landed: publish it
       wait_vmcnt<0>();
       wait_lds_reads();
       barrier();
-      // scales of chunk c+1 replace those of chunk c-1 while block 8c is computed
-      if (b % SCS == 0 && b > 0) {
-        const int cb = ((b / SCS + 1) & 1) * SC_BYTES;
-        mx_issue_scales<FA, FB, KS>(smem + L::SA_REGION + cb, smem + L::SB_REGION + cb, lp, b / SCS + 1, wave);
+      if constexpr (TAIL) {
+        if (pipe && b == KB - 2) lp.b_rsrc = rsrc_b(nx, nx_live);
+      }
+      // Scale chunks. Chunk c+1 replaces chunk c-1 (read for the last time before the barrier of
+      // stage SCS c - 1) while stage SCS c is computed. A unit's first two chunks are loaded before
+      // it starts: in its prologue, or piped in the previous unit's stages KB-2 and KB-1 (into the
+      // buffers of that unit's chunks n-2 and n-1, n = its chunk count; the last one is read for
+      // the last time before the barrier of stage KB-1).
+      if constexpr (!TAIL) {
+        if (b % SCS == 0 && b > 0 && b / SCS + 1 < nchunks) {
+          const int c = b / SCS + 1, cb = ((cbase + c) & 1) * SC_BYTES;
+          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, c, wave);
+        }
+      }
+      if constexpr (TAIL) {
+        if (pipe && b == KB - 2) {
+          rsrc_scales(nx, nx_live);
+          const int cb = ((cbase + nchunks) & 1) * SC_BYTES;
+          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 0, wave);
+        }
+        if (pipe && b == KB - 1) {
+          const int cb = ((cbase + nchunks - 1) & 1) * SC_BYTES;
+          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 1, wave);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 3]));
       __builtin_amdgcn_sched_barrier(0);
-      // pass 6 with the first copies of the B half of block b+2 into stage S (past the last
-      // block they repeat block KB-1 into a stage that is not read again)
+      // pass 6 with the first copies of the B half of stage b+2 into stage S
 #pragma unroll
       for (int h = 0; h < KS; h++)
 #pragma unroll
@@ -350,12 +424,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         acc[i][NJ - 2] = mma<FA, FB>(sub_op<KS>(bq[(NJ - 2) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 2],
                                      sbq[(NJ - 2) % 3][h], sa[i][h]);
         if ((i & 1) && (i >> 1) < B_PP && h == KS - 1)
-          mx_copy_b<FA, FB, KS>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), i >> 1);
+          mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION + sob, lp, kb_b, i >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // pass 7: last B fragment; each A fragment and its scale are refilled from block b+1
-      // right after their MFMA; the rest of the B half of block b+2; then the first two B
-      // fragments of block b+1 and their scales are read
+      // pass 7: last B fragment; each A fragment and its scale are refilled from stage b+1
+      // right after their MFMA; the rest of the B half of stage b+2; then the first two B
+      // fragments of stage b+1 and their scales are read (in the unit's last stage these reads
+      // are not used: the next unit reads its first stage afresh)
 #pragma unroll
       for (int h = 0; h < KS; h++)
 #pragma unroll
@@ -370,7 +445,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 #pragma unroll
         for (int h = 0; h < KS; h++) sa[i][h] = scale_a(KS * bn + h, i);
         if ((i & 1) && (i >> 1) < B_PP)
-          mx_copy_b<FA, FB, KS>(smem + L::B_REGION + sob, lp, min(b + 2, KB - 1), B_PP + (i >> 1));
+          mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION + sob, lp, kb_b, B_PP + (i >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       bq[0] = read_frag<L::RB>(smem + L::B_REGION + snb, fb);
@@ -383,33 +458,60 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
       __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vmcnt<0>();
+    };
 
-    // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
-    // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col)
+    int b = 0;
+    for (; b + 2 < KB; b++) stage(std::false_type{}, b);
+    // the unit's last two stages (or its only one)
+    stage(std::true_type{}, b);
+    if (b + 1 < KB) stage(std::true_type{}, b + 1);
+  };
+
+  // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
+  // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col). The stores are
+  // not waited for: the next unit's first wait before a barrier covers them.
+  auto store_c = [&](const Unit& u) {
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       const int mloc = wm * WM + i * 16 + r16;
-      if (mloc >= rows) continue;
-      const size_t crow = (size_t)(row0 + mloc) * N;
+      if (mloc >= u.rows) continue;
+      const size_t crow = (size_t)(u.row0 + mloc) * N;
 #pragma unroll
       for (int jj = 0; jj < NJ / 2; jj++) {
-        const int col = n0 + wn * WN + jj * 32 + q * 8;
-        if (col < N) store8<OUT>(p.C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
+        const int col = u.n0 + wn * WN + jj * 32 + q * 8;
+        if (col < N) store8<OUT>(C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
       }
     }
-    if (ps + 1 < npass) barrier();   // every wave is past its last LDS read before the next pass
+  };
+
+  // The persistent loop: units of items xb, xb + G, ..., one pipeline through all.
+  UnitSeq seq;
+  seq.L = xb - (int)gridDim.x;
+  seq.k = 0;
+  Unit cu, nx = {0, 0, 0, 0};
+  bool have = next_unit(p, tm, n_blocks, items, seq, cu);
+  bool have_next = have && next_unit(p, tm, n_blocks, items, seq, nx);
+  for (bool first = true; have; first = false) {
+    if (!first && !piped) barrier();   // every wave is past its last LDS read of the previous unit
+    run_unit(cu, first || !piped, piped, nx, have_next && piped);
+    store_c(cu);
+    if (!have_next) break;
+    cbase = (cbase + nchunks) & 1;
+    cu = nx;
+    have_next = next_unit(p, tm, n_blocks, items, seq, nx);
   }
 }
 
 template <int FA, int FB, int KS = 1>
 hipError_t launch_fmt(const GemmArgs& a, int out, hipStream_t stream, dim3 grid, int n_blocks) {
   dim3 block(NTHREADS);
+  const int32_t* eids = a.expert_ids;
+  const int32_t* toffs = a.tile_offsets;
+  void* c = a.C;
   switch (out) {
-    case kOutF32: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF32, KS>), grid, block, 0, stream, a, n_blocks); break;
-    case kOutBF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutBF16, KS>), grid, block, 0, stream, a, n_blocks); break;
-    case kOutF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF16, KS>), grid, block, 0, stream, a, n_blocks); break;
+    case kOutF32: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF32, KS>), grid, block, 0, stream, a, n_blocks, eids, toffs, c); break;
+    case kOutBF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutBF16, KS>), grid, block, 0, stream, a, n_blocks, eids, toffs, c); break;
+    case kOutF16: hipLaunchKernelGGL((mx_kernel<FA, FB, kOutF16, KS>), grid, block, 0, stream, a, n_blocks, eids, toffs, c); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -417,12 +519,17 @@ hipError_t launch_fmt(const GemmArgs& a, int out, hipStream_t stream, dim3 grid,
 
 }  // namespace
 
-hipError_t launch_mx(const GemmArgs& a, int fmt_a, int fmt_b, int out, hipStream_t stream) {
-  const int n_blocks = (a.N + BN - 1) / BN;
-  const long long blocks = (long long)((a.num_tiles + 1) / 2) * n_blocks;
+hipError_t launch_mx(const GemmArgs& a0, int fmt_a, int fmt_b, int out, hipStream_t stream) {
+  const int n_blocks = (a0.N + BN - 1) / BN;
+  const long long blocks = (long long)((a0.num_tiles + 1) / 2) * n_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0LL) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(blocks));
+  // persistent grid: one workgroup per compute unit (the LDS ring allows one), fewer when there
+  // are fewer items; a multiple of 8 for the XCD-aware order. Work order groups as in the
+  // blockwise kernel: 8 super-tiles, or 1 when there are at most 8 column blocks.
+  const dim3 grid(grid_for(blocks < a0.num_cus ? blocks : a0.num_cus));
+  GemmArgs a = a0;
+  a.group_m = n_blocks <= 8 ? 1 : 8;
   if (fmt_a == 1 && fmt_b == 1) return launch_fmt<1, 1>(a, out, stream, grid, n_blocks);
   if (fmt_a == 1 && fmt_b == 2) return launch_fmt<1, 2>(a, out, stream, grid, n_blocks);
   if (fmt_a == 2 && fmt_b == 1) return launch_fmt<2, 1>(a, out, stream, grid, n_blocks);
