@@ -61,7 +61,7 @@ METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 # HBM bytes per gate_up launch: rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
 # 1 GiB device copy measured with the same counters). Valid only for the kernel source whose
 # sha256 starts with this prefix; reported as null for any other source.
-GATE_UP_TRAFFIC = ("f22ccf302c696378", 11.94e9)
+GATE_UP_TRAFFIC = ("2013bd1f66d0297f", 11.75e9)
 KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
 
 
@@ -69,7 +69,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_groupe
 # prefix of that source, HBM bytes per launch).
 SINGLE_TRAFFIC = {
     "nvfp4_8192": ("nv_fp4.hip", "0c838a70d41842ac", 0.590e9),
-    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "20af0c6fd2092647", 0.991e9),
+    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "5b31a914dc5e9800", 1.000e9),
 }
 
 
