@@ -70,6 +70,8 @@ constexpr int LDS_BYTES = AS_REGION + 2 * AS_BYTES;          // 148480 of 160 Ki
 constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;             // 4
 constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;             // 4
 constexpr int AS_INSTR = AS_BYTES / 256 / NWAVES;            // 4 (4-byte copies, 64 lanes)
+// forms of the K loop (see k_loop)
+constexpr int MODE_IDLE = 0, MODE_FULL = 1, MODE_HALF = 2;
 
 // Buffer resources of one unit of work (one pass of a work item over its rows): A rows, the
 // expert's B rows of the column block, this wave's B scales and the A scales of the rows. A unit
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
   // them). pipe: the last two blocks copy the first blocks of unit nx (zero-byte resources unless
   // nx_live), which must then start at block 0; needs kend - kb0 even.
   auto run_unit = [&](const Unit& u, const int kb0, const int kend, const bool prologue, const bool pipe,
-                      const Unit& nx, const bool nx_live) {
+                      const Unit& nx, const bool nx_live, const bool half) {
     const int rows = u.rows;
     const int nb = kend - kb0;
     const int c0 = kb0 / AS_CHUNK, cl = (kend - 1) / AS_CHUNK;   // first and last chunk of the unit
@@ -299,28 +301,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       barrier();
     }
 
-      // The K loop, in two forms. A wave whose 64 rows all lie past the unit's rows (the upper half
-      // of a 128-row pass) runs it without reads, MFMAs or promotion: it still issues its copies
-      // and reaches every barrier, so both forms keep the same sequence of waits and barriers.
-      auto k_loop = [&](auto active_tag) {
-      constexpr bool ACT = decltype(active_tag)::value;
+      // The K loop, in three forms (MODE). FULL: the wave's 64 x 128 of a pass of more than 128
+      // rows. IDLE: a wave with nothing to compute (its rows lie past the pass) runs the loop
+      // without reads, MFMAs or promotion. HALF: a pass of at most 128 rows is split over the 8
+      // waves as 2 x 4 tiles of 64 x 64 (rows 64 (w / 4), columns 64 (w % 4)), so each SIMD keeps
+      // two waves of matrix work instead of one. Every form issues the same copies at the same
+      // points and reaches every barrier, so all keep one sequence of waits and barriers.
+      auto k_loop = [&](auto mode_tag) {
+      constexpr int MODE = decltype(mode_tag)::value;
+      constexpr bool ACT = MODE != MODE_IDLE;
+      constexpr int SL = MODE == MODE_HALF ? 2 : MI;    // MFMA slots per pass (8 passes per block)
+      constexpr int NK = 8 * SL;                        // MFMAs per block
+      // per-lane LDS read bases of this form (HALF: formed here and made opaque, so that they are
+      // not kept live through the other forms)
+      int ba[2], bb[2], bas;
+      int bbs = base_bs;
+      if constexpr (MODE == MODE_HALF) {
+        const int hm = wave >> 2, hq = wave & 3;
+  #pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int chunk = ((2 * q + h) ^ sw) * 16;
+          ba[h] = A_REGION + (hm * WM + r16) * BK + chunk;
+          bb[h] = B_REGION + ((hq >> 1) * 128 + (hq & 1) * 64 + r16) * BK + chunk;
+        }
+        bas = (AS_REGION + (hm * WM + r16) * AS_CHUNK * 4) | ((r16 >> 3) << 2);
+        bbs = BS_REGION + (hq >> 1) * 256;
+        asm volatile("" : "+v"(ba[0]), "+v"(ba[1]), "+v"(bb[0]), "+v"(bb[1]), "+v"(bas));
+      } else {
+        ba[0] = base_a[0];
+        ba[1] = base_a[1];
+        bb[0] = base_b[0];
+        bb[1] = base_b[1];
+        bas = base_as;
+      }
       v8i af[MI], bq[3];
       float as_raw[MI], bs_raw = 0.f;
       if constexpr (ACT) {
   #pragma unroll
-        for (int i = 0; i < MI; i++) af[i] = read_frag(smem + i * 2048, base_a);
-        bq[0] = read_frag(smem, base_b);
-        bq[1] = read_frag(smem + 2048, base_b);
-        const int as0 = (base_as ^ ((kb0 % AS_CHUNK) * 4)) + (cbase & 1) * AS_BYTES;
+        for (int i = 0; i < MI; i++) af[i] = read_frag(smem + i * 2048, ba);
+        bq[0] = read_frag(smem, bb);
+        bq[1] = read_frag(smem + 2048, bb);
+        const int as0 = (bas ^ ((kb0 % AS_CHUNK) * 4)) + (cbase & 1) * AS_BYTES;
   #pragma unroll
         for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + (as0 ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
-        bs_raw = *(const float*)(smem + base_bs);
+        bs_raw = *(const float*)(smem + bbs);
       }
 
       // One K block (kb, the r-th of the unit). S (its stage) is a constant so every LDS offset is
       // an immediate. Blocks of the main loop (TAIL false) copy from the current unit only; the last
       // two blocks (TAIL true) copy the next unit's first blocks when piped, else repeat block
-      // kend-1 into a stage that is not read again.
+      // kend-1 into a stage that is not read again. MFMA k of a block multiplies B fragment k / MI
+      // by A fragment k % MI (FULL: 8 B fragments over 8 passes of 4; HALF: 4 over 8 passes of 2).
       auto k_block = [&](auto stage_tag, auto tail_tag, const int r) {
         const int b = kb0 + r;
         constexpr int S = decltype(stage_tag)::value;
@@ -348,41 +379,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           for (int i = 0; i < MI; i++) sc[i] = as_raw[i] * bs_raw;
         }
         v4f part[4];
-        // passes 0..5: B fragment j against the 4 resident A fragments, at raised wave priority so
-        // the SIMD's arbiter favours feeding the matrix unit; B fragment j + 2 is read in two
-        // halves, after the first and the third MFMA. The promotion of each partial is pinned
-        // right after the MFMA three slots later, which also keeps the MFMAs in their pass. Passes 0
+        // the MFMA of slot k, and the promotion of the partial three slots back (pinned there,
+        // which also keeps the MFMAs in their pass)
+        auto mfma_slot = [&](const int k) {
+          part[k % 4] = mma(bq[(k / MI) % 3], af[k % MI]);
+          if (k >= 3) {
+            const int kp = k - 3, jp = kp / MI, ip = kp % MI;
+            acc[ip][jp] += part[kp % 4] * sc[ip];
+            asm volatile("" : "+v"(acc[ip][jp]));
+          }
+        };
+        // passes 0..5 at raised wave priority so the SIMD's arbiter favours feeding the matrix
+        // unit. Reads of the B fragments two ahead (FULL: fragment j + 2 in two halves, after the
+        // first and the third MFMA of pass j; HALF: fragments 2 and 3 in passes 0 and 2). Passes 0
         // and 1 also copy the A half and B scales of block b+1 into the other stage (freed by the
-        // barrier of block b-1; its B half went out in passes 6 and 7 of block b-1).
+        // barrier of block b-1; its B half went out in passes 6 and 7 of block b-1), two copies per
+        // pass.
   #pragma unroll
-        for (int j = 0; j < NJ - 2; j++) {
+        for (int j = 0; j < 6; j++) {
           __builtin_amdgcn_sched_barrier(0);
           v4i lo, hi;
           __builtin_amdgcn_s_setprio(1);
   #pragma unroll
-          for (int i = 0; i < MI; i++) {
-            const int k = j * MI + i;
-            if constexpr (ACT) {
-              part[k % 4] = mma(bq[j % 3], af[i]);
-              if (k >= 3) {
-                const int kp = k - 3, jp = kp / MI, ip = kp % MI;
-                acc[ip][jp] += part[kp % 4] * sc[ip];
-                asm volatile("" : "+v"(acc[ip][jp]));
-              }
+          for (int i = 0; i < SL; i++) {
+            if constexpr (ACT) mfma_slot(j * SL + i);
+            if (j < 2 && (MODE == MODE_HALF || (i & 1))) {
+              copy_a(lb.wb + A_REGION + sn_ab, rc.a, cp, kb_a, MODE == MODE_HALF ? 2 * j + i : 2 * j + (i >> 1));
+              if (j == 1 && i == SL - 1) copy_bs(lb.wbs + sn_bs, rc.bs, kb_a, wave);
             }
-            if (j < 2 && (i & 1)) {
-              copy_a(lb.wb + A_REGION + sn_ab, rc.a, cp, kb_a, 2 * j + (i >> 1));
-              if (j == 1 && i == 3) copy_bs(lb.wbs + sn_bs, rc.bs, kb_a, wave);
-            }
-            if constexpr (ACT) {
-              if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[0]);
-              if (j + 2 < NJ && i == 2) hi = lds_read16(smem + so_ab + (j + 2) * 2048 + base_b[1]);
+            if constexpr (MODE == MODE_FULL) {
+              if (j + 2 < NJ && i == 0) lo = lds_read16(smem + so_ab + (j + 2) * 2048 + bb[0]);
+              if (j + 2 < NJ && i == 2) hi = lds_read16(smem + so_ab + (j + 2) * 2048 + bb[1]);
+            } else if constexpr (MODE == MODE_HALF) {
+              if ((j == 0 || j == 2) && i == 0) lo = lds_read16(smem + so_ab + (j / 2 + 2) * 2048 + bb[0]);
+              if ((j == 0 || j == 2) && i == 1) hi = lds_read16(smem + so_ab + (j / 2 + 2) * 2048 + bb[1]);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
           __builtin_amdgcn_s_setprio(0);
-          if constexpr (ACT) {
+          if constexpr (MODE == MODE_FULL) {
             if (j + 2 < NJ) bq[(j + 2) % 3] = cat(lo, hi);
+          } else if constexpr (MODE == MODE_HALF) {
+            if (j == 0 || j == 2) bq[(j / 2 + 2) % 3] = cat(lo, hi);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -395,18 +433,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           if (pipe && b == kend - 2) rc.b = rsrc_b(p, nx, nx_live);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // pass 6 (B fragment 6, no reads left in this block) with copies 0 and 1 of the B half of
-        // block b+2 into stage S
+        // pass 6 (no reads left in this block) with copies 0 and 1 of the B half of block b+2 into
+        // stage S; HALF: the MFMAs of pass 6 are the last of A fragments 0 and 1, which are
+        // refilled from block b+1 right after them
   #pragma unroll
-        for (int i = 0; i < MI; i++) {
-          const int k = (NJ - 2) * MI + i;
+        for (int i = 0; i < SL; i++) {
           if constexpr (ACT) {
-            part[k % 4] = mma(bq[(NJ - 2) % 3], af[i]);
-            const int kp = k - 3, jp = kp / MI, ip = kp % MI;
-            acc[ip][jp] += part[kp % 4] * sc[ip];
-            asm volatile("" : "+v"(acc[ip][jp]));
+            mfma_slot(6 * SL + i);
+            if constexpr (MODE == MODE_HALF) af[i] = read_frag(smem + sn_ab + i * 2048, ba);
           }
-          if (i & 1) copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, i >> 1);
+          if (MODE == MODE_HALF || (i & 1)) copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, MODE == MODE_HALF ? i : i >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
         // A scale chunks. Chunk c (blocks 8c .. 8c+7) goes into its buffer in block 8(c-1), when
@@ -430,37 +466,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
             issue_scale_chunk(lb.wch + ((cbase + cl - c0) & 1) * AS_BYTES, rc.as, cp, 1, wave);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // pass 7: the last B fragment; each A fragment is refilled from block b+1 right after its
-        // MFMA, then the first two B fragments and the scales of block b+1 are read; copies 2 and 3
-        // of the B half of block b+2.
+        // pass 7: the last MFMAs of the other A fragments (all four in FULL), each refilled from
+        // block b+1 right after its MFMA, then the first two B fragments and the scales of block
+        // b+1 are read; copies 2 and 3 of the B half of block b+2.
   #pragma unroll
-        for (int i = 0; i < MI; i++) {
-          const int k = (NJ - 1) * MI + i;
+        for (int i = 0; i < SL; i++) {
           if constexpr (ACT) {
-            part[k % 4] = mma(bq[(NJ - 1) % 3], af[i]);
-            const int kp = k - 3, jp = kp / MI, ip = kp % MI;
-            acc[ip][jp] += part[kp % 4] * sc[ip];
-            asm volatile("" : "+v"(acc[ip][jp]));
-            af[i] = read_frag(smem + sn_ab + i * 2048, base_a);
+            const int k = 7 * SL + i;
+            mfma_slot(k);
+            af[k % MI] = read_frag(smem + sn_ab + (k % MI) * 2048, ba);
           }
-          if (i & 1) copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, 2 + (i >> 1));
+          if (MODE == MODE_HALF || (i & 1))
+            copy_b(lb.wb + B_REGION + so_ab, rc.b, cp, kb_b, MODE == MODE_HALF ? 2 + i : 2 + (i >> 1));
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (ACT) {
-          bq[0] = read_frag(smem + sn_ab, base_b);
-          bq[1] = read_frag(smem + sn_ab + 2048, base_b);
+          bq[0] = read_frag(smem + sn_ab, bb);
+          bq[1] = read_frag(smem + sn_ab + 2048, bb);
           const int bn = min(b + 1, kend - 1);
-          const int as_v = (base_as ^ ((bn % AS_CHUNK) * 4)) + ((cbase + bn / AS_CHUNK - c0) & 1) * AS_BYTES;
+          const int as_v = (bas ^ ((bn % AS_CHUNK) * 4)) + ((cbase + bn / AS_CHUNK - c0) & 1) * AS_BYTES;
   #pragma unroll
           for (int i = 0; i < MI; i++)
             as_raw[i] = *(const float*)(smem + (as_v ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
-          bs_raw = *(const float*)(smem + sn_bs + base_bs);
+          bs_raw = *(const float*)(smem + sn_bs + bbs);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the last three partials of the block
         if constexpr (ACT) {
   #pragma unroll
-          for (int k = MI * NJ - 3; k < MI * NJ; k++) {
+          for (int k = NK - 3; k < NK; k++) {
             const int jp = k / MI, ip = k % MI;
             acc[ip][jp] += part[k % 4] * sc[ip];
             asm volatile("" : "+v"(acc[ip][jp]));
@@ -479,26 +513,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       k_block(S0{}, std::true_type{}, r);
       if (r + 1 < nb) k_block(S1{}, std::true_type{}, r + 1);
       };
-      if (wm * WM < rows)
-        k_loop(std::true_type{});
-      else
-        k_loop(std::false_type{});
+      if (half && rows <= TILE_M) {
+        if ((wave >> 2) * WM < rows)
+          k_loop(std::integral_constant<int, MODE_HALF>{});
+        else
+          k_loop(std::integral_constant<int, MODE_IDLE>{});
+      } else if (wm * WM < rows) {
+        k_loop(std::integral_constant<int, MODE_FULL>{});
+      } else {
+        k_loop(std::integral_constant<int, MODE_IDLE>{});
+      }
 
   };
 
   // epilogue: lane holds row r16 of each M fragment and, over N fragments 2 jj and 2 jj + 1,
-  // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col). The stores are
-  // not waited for: the next unit's first wait before a barrier covers them.
-  auto store_c = [&](const Unit& u) {
+  // columns 32 jj + 8 q .. 32 jj + 8 q + 7 of its 128-column block (see b_col); in the HALF form
+  // (a pass of at most 128 rows) the wave's 64 columns start at 128 (w % 4 / 2) + 64 (w % 2) and
+  // its rows at 64 (w / 4). The stores are not waited for: the next unit's first wait before a
+  // barrier covers them.
+  auto store_c = [&](const Unit& u, const bool half) {
+    const int hm = half ? wave >> 2 : wm;
+    const int cw = half ? ((wave & 3) >> 1) * 128 + (wave & 1) * 64 : wn * WN;
+    const int nf = half ? 2 : NJ / 2;
 #pragma unroll
     for (int i = 0; i < MI; i++) {
-      const int mloc = wm * WM + i * 16 + r16;
+      const int mloc = hm * WM + i * 16 + r16;
       if (mloc >= u.rows) continue;
       const size_t crow = (size_t)(u.row0 + mloc) * N;
 #pragma unroll
       for (int jj = 0; jj < NJ / 2; jj++) {
-        const int col = u.n0 + wn * WN + jj * 32 + q * 8;
-        if (col < N) store8<OUT>(C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
+        const int col = u.n0 + cw + jj * 32 + q * 8;
+        if (jj < nf && col < N) store8<OUT>(C, crow + col, acc[i][2 * jj], acc[i][2 * jj + 1]);
       }
     }
   };
@@ -513,8 +558,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     bool have_next = have && next_unit(p, tm, n_blocks, items_dp, seq, nx);
     for (bool first = true; have; first = false) {
       if (!first && !piped) barrier();   // every wave is past its last LDS read of the previous unit
-      run_unit(cu, 0, KB, first || !piped, piped, nx, have_next && piped);
-      store_c(cu);
+      const bool half = cu.rows <= TILE_M;
+      run_unit(cu, 0, KB, first || !piped, piped, nx, have_next && piped, half);
+      store_c(cu, half);
       if (!have_next) break;
       cbase = (cbase + nchunks) & 1;
       cu = nx;
@@ -551,7 +597,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       w.rows = __builtin_amdgcn_readfirstlane(w.rows);
       w.n0 = __builtin_amdgcn_readfirstlane(w.n0);
       if (ps > 0) barrier();   // every wave is past its last LDS read of the previous pass
-      run_unit(w, kb0, kend, true, false, w, false);   // never piped
+      run_unit(w, kb0, kend, true, false, w, false, false);   // never piped, never HALF
       // partial tile: per (wave, pass) 32 x 1 KiB, lane-contiguous; a pass of an item of two
       // passes has at most 128 rows (waves 0-3), so its second pass uses waves 4-7's space
       if (wm * WM < w.rows) {
