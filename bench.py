@@ -371,26 +371,39 @@ def bench_permute(args, torch, bsg):
 
 
 def bench_decode(args, torch, bsg):
-    """A step: the gate_up grouped GEMM of a 128-token decode batch, small-M schedule."""
-    from workloads.generate import blockwise_problem, routing_counts
+    """A step: the gate_up grouped GEMM of a 128-token decode batch, small-M schedule, with A in the
+    compact layout (each expert's rows packed, so an expert's last M-tile is partial and the
+    small-M kernel stops at its last 16-row fragment). The padded layout (every group a multiple
+    of 128 rows) and the large-tile schedule are timed alongside for reference."""
+    from workloads.generate import blockwise_problem, padded_starts, routing_counts
 
     route = dict(tokens=128, top_k=8, experts=32, alpha=1.0, n_empty=2)
     counts = routing_counts(seed=args.seed, **route)
     N, K, E = 4096, 7168, 32
     p = blockwise_problem(list(int(c) for c in counts), N, K, device="cuda", seed=args.seed)
     c = torch.tensor(counts, dtype=torch.int32, device="cuda")
-    T = p.M // 128
-    _, to, ei = bsg.bsgemm_build_tiles(c, T, padded=True)
-    C = torch.empty(p.M, N, dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
     active = int(np.count_nonzero(counts))
     real = int(np.sum(counts))
-    nbytes = (active * N * K + active * (N // 128) * (K // 128) * 4      # B and its scales
-              + p.M * K + p.M * (K // 128) * 4 + real * N * 2)            # A, a_scales, C rows
+    # the same rows packed: expert e's real rows of the padded A, one group after another
+    starts = padded_starts(counts)
+    keep = torch.as_tensor(np.concatenate([np.arange(starts[e], starts[e] + counts[e]) for e in range(E)]),
+                           dtype=torch.int64, device="cuda")
+    layouts = {}
+    for name, qa, sa, M, padded in (("padded", p.qa, p.a_scales, p.M, True),
+                                    ("compact", p.qa[keep].contiguous(), p.a_scales[keep].contiguous(), real, False)):
+        T = int(sum(-(-int(x) // 128) for x in counts)) if not padded else p.M // 128
+        _, to, ei = bsg.bsgemm_build_tiles(c, T, padded=padded)
+        layouts[name] = (qa, sa, M, T, to, ei, torch.empty(M, N, dtype=torch.bfloat16, device="cuda"))
+    stream = torch.cuda.current_stream()
 
-    def time_fmt(small, steps, warmup):
+    def nbytes_of(M):
+        return (active * N * K + active * (N // 128) * (K // 128) * 4     # B and its scales
+                + M * K + M * (K // 128) * 4 + real * N * 2)               # A, a_scales, C rows
+
+    def time_fmt(layout, small, steps, warmup):
+        qa, sa, M, T, to, ei, C = layouts[layout]
         fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16", small_m=small)
-        call = lambda: bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei, to, C, p.M, N, K,
+        call = lambda: bsg.bsgemm_grouped(qa, sa, p.qb, p.b_scales, ei, to, C, M, N, K,
                                           fmt, num_experts=E, stream=stream)
         for _ in range(warmup):
             call()
@@ -407,10 +420,15 @@ def bench_decode(args, torch, bsg):
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return wall, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    large_wall, large_ms = time_fmt(False, args.steps, args.warmup)
-    ms_per_step, call_ms = time_fmt(True, args.steps, args.warmup)
+    times = {}
+    for layout in ("padded", "compact"):
+        for small in (False, True):
+            times[(layout, small)] = time_fmt(layout, small, args.steps, args.warmup)
+    ms_per_step, call_ms = times[("compact", True)]
+    nbytes = nbytes_of(real)
     achieved = nbytes / (call_ms * 1e-3) / 1e9
     value = nbytes / (ms_per_step * 1e-3) / 1e9
+    T_c, T_p = layouts["compact"][3], layouts["padded"][3]
     out = {
         "metric": "GB/s, grouped blockwise-FP8 GEMM for a decode batch (B streamed once per expert)",
         "value": round(value, 1), "unit": "GB/s", "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -418,18 +436,21 @@ def bench_decode(args, torch, bsg):
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
         "config": {"workload": f"decode_moe32: 128 tokens x top-8 over 32 experts (Dirichlet(1.0), "
-                               f"2 empty) = {real} rows in {T} M-tiles; gate_up N={N}, K={K}; bf16 out",
-                   "tokens": 128, "top_k": 8, "experts": E, "rows": real, "m_tiles": T, "seed": args.seed},
-        "kernels_ms": {"small_m_schedule": round(call_ms, 4), "large_tile_schedule": round(large_ms, 4)},
+                               f"2 empty) = {real} rows, compact layout ({T_c} M-tiles; padded: {T_p}); "
+                               f"gate_up N={N}, K={K}; bf16 out",
+                   "tokens": 128, "top_k": 8, "experts": E, "rows": real, "m_tiles": T_c, "seed": args.seed},
+        "kernels_ms": {f"{layout}_{'small_m' if small else 'large_tile'}": round(t[1], 4)
+                       for (layout, small), t in times.items()},
         "useful_tflops": round(2.0 * real * N * K / (call_ms * 1e-3) / 1e12, 1),
         "roofline": {
-            "kernel": "bw_fp8_small_m_kernel (gate_up, decode batch)", "bound": "hbm",
+            "kernel": "bw_fp8_small_m_kernel (gate_up, decode batch, compact layout)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_decode(p, counts, ei, to, nbytes)
+        qa, sa, M, T, to, ei, _ = layouts["padded"]
+        out["cpu_baseline"] = cpu_baseline_decode(p, counts, ei, to, nbytes_of(p.M))
     print(json.dumps(out), flush=True)
 
 
