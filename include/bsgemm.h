@@ -166,13 +166,16 @@ int bsgemm_grouped_workspace_size(size_t* bytes);
  * cut each item along K into 2-16 equal ranges of at least 8 K blocks (as many as the grid
  * holds) that run side by side: each range accumulates its K blocks as described under
  * bsgemm_grouped into an fp32 partial tile, and the item's result is the sum of its ranges'
- * partials (each range sums and stores a slice of the tile). Problems with at least as many
- * items as compute units, formats other than blockwise, and the small-M hint run exactly as
- * bsgemm_grouped and leave the workspace untouched.
+ * partials (each range sums and stores a slice of the tile). Blockwise problems with at least as
+ * many items as compute units run whole items as bsgemm_grouped does, bit for bit; when K is at
+ * least 5120 (40 K blocks) they take the items of each XCD from a counter in the workspace's
+ * first 32 bytes (cleared on the stream before the launch) instead of a fixed sequence, which
+ * keeps the items in flight on an XCD close together in the work order. Formats other than
+ * blockwise and the small-M hint run exactly as bsgemm_grouped and leave the workspace untouched.
  *
  *   workspace        DEVICE, 256-byte aligned, at least bsgemm_grouped_workspace_size bytes,
- *                    owned by the caller; no initial contents are required (its flags are
- *                    cleared on the stream before each split launch). Its int32 word 1023 is
+ *                    owned by the caller; no initial contents are required (what a launch
+ *                    uses of it is cleared on the stream before the launch). Its int32 word 1023 is
  *                    an error word: nonzero after a call if a range ever stopped waiting for the
  *                    other ranges of its item (not expected while the call has the GPU's compute
  *                    units to itself; that item's output is then wrong).
@@ -196,8 +199,8 @@ int bsgemm_grouped_ws(const void* A, const void* a_scales, const void* B, const 
  * array the library holds on each device it runs on, for the life of the process: 16 MiB + 4 KiB,
  * room for 64 partial tiles. Where bsgemm_grouped_ws would cut the items into more ranges than
  * 64 tiles, fewer ranges are used, so no call needs more scratch than the array holds and none
- * is rejected for it (results are within the same tolerance). The scratch's flags are cleared on
- * the stream at the start of every split launch.
+ * is rejected for it (results are within the same tolerance). What a launch uses of the scratch
+ * (the split schedule's flags, the work-order counters) is cleared on the stream before it.
  * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU (different streams
  * or host threads without ordering) race and give wrong results. No hipMalloc, hipFree or other
  * allocating call is made.

@@ -127,3 +127,60 @@ def test_large_problem_runs_whole_items(workspace):
     bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C2, p.M, p.N, p.K,
                        bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16"))
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+def _dyn_applies(tiles, N, K):
+    """The library's rule for the dynamic work order (whole items through the workspace)."""
+    G = num_cus() // 8 * 8
+    return items_of(tiles, N) >= G and K // 128 >= 40 and split_parts(tiles, N, K) == 1
+
+
+def _static_and_ws(p, ei, to, out, ws, calls=2):
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", out)
+    nt = None if ei is None else ei.numel()
+    C_static = poisoned(p.M, p.N, out)
+    bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, ei, to, C_static, p.M, p.N, p.K, fmt,
+                       num_tiles=nt, num_experts=p.E)
+    outs = []
+    for _ in range(calls):   # calls in a row on one workspace: the counters are cleared each time
+        C = poisoned(p.M, p.N, out)
+        bsg.bsgemm_grouped_ws(p.qa, p.a_scales, p.qb, p.b_scales, ei, to, C, p.M, p.N, p.K, fmt, ws,
+                              num_tiles=nt, num_experts=p.E)
+        outs.append(C)
+    torch.cuda.synchronize()
+    return C_static, outs
+
+
+def test_dynamic_work_order_dense_bit_identical(workspace):
+    """8192 x 2048 x 5120 (256 items of 40 K blocks): the workspace call takes each XCD's items
+    from a counter; every item is computed as in bsgemm_grouped, so the output is the same bit for
+    bit (and within the oracle's tolerance on sampled rows)."""
+    p = blockwise_problem(None, 2048, 5120, device="cuda", a_rows=8192, seed=51)
+    assert _dyn_applies(p.M // 128, p.N, p.K)
+    C_static, outs = _static_and_ws(p, None, None, "bf16", workspace)
+    for C in outs:
+        assert torch.equal(C.view(torch.int16), C_static.view(torch.int16))
+    check(p, "bf16", outs[-1], rows=sample_rows(p), label="dynamic order dense")
+
+
+def test_dynamic_work_order_grouped_with_skipped_items(workspace):
+    """Ragged groups of 40 experts at K = 5120 with every fourth super-tile's tiles given an
+    out-of-range expert id: items without a live tile are taken and passed over (the counter is
+    asked again), their rows stay untouched, and everything matches bsgemm_grouped bit for bit."""
+    rng = np.random.default_rng(11)
+    counts = rng.integers(0, 4000, 40)
+    counts[[2, 9]] = 0
+    p = blockwise_problem([int(c) for c in counts], 256, 5120, device="cuda", seed=52)
+    T = p.M // 128
+    assert _dyn_applies(T, p.N, p.K)
+    _, to, ei = gpu_tile_map(p.counts, T)
+    ei = ei.clone()
+    ei.view(-1)[0::8] = 1000     # both tiles of every fourth super-tile: expert out of range
+    ei.view(-1)[1::8] = -1
+    C_static, outs = _static_and_ws(p, ei, to, "bf16", workspace)
+    for C in outs:
+        assert torch.equal(C.view(torch.int16), C_static.view(torch.int16))
+    ei_h = ei.cpu().numpy().copy()
+    ei_h[(ei_h < 0) | (ei_h >= p.E)] = -1
+    check(p, "bf16", outs[-1], rows=sample_rows(p), tile_map_ref=(ei_h, to.cpu().numpy()),
+          label="dynamic order with skipped items")

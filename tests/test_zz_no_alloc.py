@@ -48,3 +48,19 @@ def test_noalloc_matches_workspace_entry_two_calls():
                                 C_ws.float().cpu().numpy().astype(np.float64), den)
         say(f"[no-alloc] {label}: vs workspace entry point max_rel_err={err:.3e}")
         assert err <= TOL[out]
+
+
+def test_noalloc_dynamic_work_order_bit_identical():
+    """Whole items of 40 K blocks or more (8192 x 2048 x 5120: 256 items): the no-alloc call takes
+    each XCD's items from counters in the library's scratch; two calls in a row, each equal bit for
+    bit to bsgemm_grouped (same per-item arithmetic)."""
+    p = blockwise_problem(None, 2048, 5120, device="cuda", a_rows=8192, seed=61)
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
+    C_ref = poisoned(p.M, p.N, "bf16")
+    bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C_ref, p.M, p.N, p.K, fmt)
+    for call in (1, 2):
+        C = poisoned(p.M, p.N, "bf16")
+        bsg.bsgemm_grouped_noalloc(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C, p.M, p.N, p.K, fmt)
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int16), C_ref.view(torch.int16)), f"call {call}"
+        say(f"[no-alloc] dynamic order call {call}: bit-identical")
