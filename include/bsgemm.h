@@ -167,18 +167,26 @@ int bsgemm_grouped_workspace_size(size_t* bytes);
  * holds) that run side by side: each range accumulates its K blocks as described under
  * bsgemm_grouped into an fp32 partial tile, and the item's result is the sum of its ranges'
  * partials (each range sums and stores a slice of the tile). Blockwise problems with at least as
- * many items as compute units run whole items as bsgemm_grouped does, bit for bit; when K is at
- * least 5120 (40 K blocks) they take the items of each XCD from a counter in the workspace's
- * first 32 bytes (cleared on the stream before the launch) instead of a fixed sequence, which
- * keeps the items in flight on an XCD close together in the work order. Formats other than
- * blockwise and the small-M hint run exactly as bsgemm_grouped and leave the workspace untouched.
+ * many items as compute units run whole items as bsgemm_grouped does, bit for bit, with two
+ * exceptions that use the workspace's first 4 KiB as counters and flags (cleared on the stream
+ * before the launch):
+ *  - when K is at least 5120 (40 K blocks), the workgroups take the items of each XCD from a
+ *    counter instead of a fixed sequence, which keeps the items in flight on an XCD close
+ *    together in the work order (same per-item arithmetic: still bit for bit);
+ *  - with fewer than 4 items per compute unit, the items of the last, partial round (items modulo
+ *    the grid) are cut along K into 2-16 ranges of at least 4 K blocks, which the workgroups that
+ *    run out of whole items first take from a counter, summed as above; outputs of those items
+ *    are within the tolerance, not bit-identical to bsgemm_grouped, and the same on every call.
+ * Formats other than blockwise and the small-M hint run exactly as bsgemm_grouped and leave the
+ * workspace untouched.
  *
  *   workspace        DEVICE, 256-byte aligned, at least bsgemm_grouped_workspace_size bytes,
  *                    owned by the caller; no initial contents are required (what a launch
  *                    uses of it is cleared on the stream before the launch). Its int32 word 1023 is
  *                    an error word: nonzero after a call if a range ever stopped waiting for the
  *                    other ranges of its item (not expected while the call has the GPU's compute
- *                    units to itself; that item's output is then wrong).
+ *                    units to itself: the ranges wait for ranges that running workgroups have
+ *                    taken; that item's output is then wrong).
  *   workspace_bytes  its size
  * Calls that share a workspace must be ordered (one stream, or synchronised): concurrent calls
  * on one workspace race.

@@ -187,17 +187,34 @@ constexpr int SC_AGENT = 16;
 
 struct SplitArgs {
   int items_dp;   // items [0, items_dp) are whole; the rest are split along K
-  int parts;      // K ranges per split item (a power of 2)
+  int parts;      // K ranges per split item (a power of 2, at most 16; 1: no item is split)
   uint8_t* ws;
   int* queue;     // whole items: 8 zeroed counters for the dynamic work order, or nullptr (static)
 };
+
+// Words of the workspace's first 4 KiB used by the launch of whole items: the dynamic order's 8
+// counters (words 0-7), the counter of the last round's ranges (TAIL_CTR_WORD) and one flag per
+// range from TAIL_FLAG_WORD0 on. A split launch uses words 0 .. items * parts - 1 as its flags.
+constexpr int TAIL_CTR_WORD = 8;
+constexpr int TAIL_FLAG_WORD0 = 16;
+// Ranges of the last round's items have at least this many K blocks, and the last round is cut
+// only in launches of fewer than TAIL_MAX_ROUNDS rounds of items. Measured over three jobs: the
+// 8-expert workload (272 items, its last 16 in 8 ranges) 0.102-0.113 -> 0.096-0.101 ms; the
+// 32-expert gate_up (33 rounds, its last 128 items in 2 ranges) 3.30-3.32 -> 3.30-3.35 ms: with
+// many rounds the workgroups' whole items already end over a spread as wide as the ranges, which
+// then only add their partial tiles' traffic.
+constexpr int TAIL_MIN_KB = 4;
+constexpr int TAIL_MAX_ROUNDS = 4;
 
 // The dynamic work order (whole items, when the launch has a workspace): the grid's workgroups
 // take the items of each XCD from a counter of that XCD instead of a fixed sequence. Items of at
 // least this many K blocks use it (see the kernel's phase 1 and launch_blockwise_fp8_split).
 constexpr int DYNAMIC_MIN_KB = 40;
 
-template <int OUT, bool SPLIT>
+// SPLIT: the split launch (items cut along K). LAST_RANGES (whole items): after its whole items,
+// the workgroup takes ranges of the last round's items (see phase 2 below); a form of its own, so
+// that launches without it keep the smaller kernel.
+template <int OUT, bool SPLIT, bool LAST_RANGES>
 __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p, int n_blocks,
                                                                        const int32_t* __restrict__ expert_ids,
                                                                        const int32_t* __restrict__ tile_offsets,
@@ -554,6 +571,103 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     }
   };
 
+  // Sum share jp of an item's partial tiles, slots slot0 .. slot0 + P - 1, in slot order and store
+  // it: v4f entries [jp * PER, (jp + 1) * PER) of the 8 x 32 x 64 in a tile, entry jp * PER +
+  // k * 512 + tid for thread tid. Entry g is lane g % 64 of fragment (g / 64) % 32 of wave slot
+  // g / 2048 (pass ws / 4 of a two-pass item, else pass 0), as the waves wrote them. All of a
+  // thread's loads are issued before the first sum, so the share costs one memory latency.
+  auto reduce_share = [&](auto parts_tag, const Unit* u, const int np, const int slot0, const int jp) {
+    constexpr int P = decltype(parts_tag)::value;
+    constexpr int ENTRIES = 8 * MI * NJ * kWave;
+    constexpr int PER = ENTRIES / P;
+    constexpr int EPT = PER / NTHREADS;   // entries per thread
+    static_assert(PER % NTHREADS == 0, "a share is whole rows of threads");
+    const __amdgpu_buffer_rsrc_t all =
+        make_rsrc(sp.ws + SPLIT_FLAG_BYTES + (size_t)slot0 * SPLIT_SLOT_BYTES, (uint64_t)P * SPLIT_SLOT_BYTES);
+    v4f v[EPT][P];
+#pragma unroll
+    for (int k = 0; k < EPT; k++)
+#pragma unroll
+      for (int m = 0; m < P; m++)
+        v[k][m] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                              all, (uint32_t)(jp * PER + k * NTHREADS + tid) * 16,
+                                              (uint32_t)(m * SPLIT_SLOT_BYTES), SC_AGENT));
+#pragma unroll
+    for (int k = 0; k < EPT; k++) {
+      const int g = jp * PER + k * NTHREADS + tid;
+      const int wsl = g / (MI * NJ * kWave), idx = (g / kWave) % (MI * NJ), ln = g % kWave;
+      const int ps = np == 2 ? wsl >> 2 : 0;
+      const int vw = np == 2 ? wsl & 3 : wsl;          // the wave that held the entry
+      const Unit& w = ps == 0 ? u[0] : u[1];
+      const int fi = idx / NJ, fj = idx % NJ;
+      const int mloc = (vw >> 1) * WM + fi * 16 + (ln & 15);
+      const int col = w.n0 + (vw & 1) * WN + ((fj >> 1) << 5) + ((ln >> 4) << 3) + ((fj & 1) << 2);
+      if (ps >= np || mloc >= w.rows || col >= N) continue;
+      v4f sum = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < P; m++) sum += v[k][m];
+      store4<OUT>(C, (size_t)(w.row0 + mloc) * N + col, sum[0], sum[1], sum[2], sum[3]);
+    }
+  };
+
+  // Range jp of item L cut along K into `parts` ranges of blocks: run it (never piped, never HALF;
+  // the caller has passed a barrier after the workgroup's last LDS reads), write the fp32 partial
+  // tile to slot slot0 + jp of the workspace, raise flags[slot0 + jp], wait until the item's
+  // `parts` flags are up, then sum share jp (a 1/parts slice of the tile) over the item's
+  // partials and store it to C. The wait ends after a bounded number of polls, should a part
+  // ever not run, and then sets the workspace's error word (the item's output is then wrong, and
+  // reported, rather than hung).
+  auto split_part = [&](const int L, const int jp, const int parts, const int slot0, int* const flags) {
+    const int kb0 = jp * KB / parts, kend = (jp + 1) * KB / parts;
+    const int slot = slot0 + jp;
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(sp.ws + SPLIT_FLAG_BYTES + (size_t)slot * SPLIT_SLOT_BYTES, SPLIT_SLOT_BYTES);
+    Unit u[2];
+    const int np = __builtin_amdgcn_readfirstlane(item_units(p, tm, n_blocks, L, u));
+    for (int ps = 0; ps < np; ps++) {
+      Unit w = ps == 0 ? u[0] : u[1];
+      w.e = __builtin_amdgcn_readfirstlane(w.e);
+      w.row0 = __builtin_amdgcn_readfirstlane(w.row0);
+      w.rows = __builtin_amdgcn_readfirstlane(w.rows);
+      w.n0 = __builtin_amdgcn_readfirstlane(w.n0);
+      if (ps > 0) barrier();   // every wave is past its last LDS read of the previous pass
+      run_unit(w, kb0, kend, true, false, w, false, false);
+      // partial tile: per (wave, pass) 32 x 1 KiB, lane-contiguous; a pass of an item of two
+      // passes has at most 128 rows (waves 0-3), so its second pass uses waves 4-7's space
+      if (wm * WM < w.rows) {
+        const uint32_t pv = (uint32_t)(((wave + 4 * ps) * (MI * NJ * kWave) + lane) * 16);
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+#pragma unroll
+          for (int j = 0; j < NJ; j++)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[i][j]), pr, pv,
+                                                   (i * NJ + j) * kWave * 16, SC_AGENT);
+      }
+    }
+    wait_vmcnt<0>();   // this wave's partial has reached the agent's coherence point
+    barrier();
+    if (tid == 0) {
+      __hip_atomic_store(flags + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int m = 0; m < parts; m++) {
+        int spins = 0;
+        while (__hip_atomic_load(flags + slot0 + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          if (++spins > SPLIT_SPIN_LIMIT) {   // never expected: give up, record it, go on
+            __hip_atomic_store((int*)sp.ws + SPLIT_ERR_WORD, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+    }
+    barrier();
+    switch (parts) {
+      case 2: reduce_share(std::integral_constant<int, 2>{}, u, np, slot0, jp); break;
+      case 4: reduce_share(std::integral_constant<int, 4>{}, u, np, slot0, jp); break;
+      case 8: reduce_share(std::integral_constant<int, 8>{}, u, np, slot0, jp); break;
+      default: reduce_share(std::integral_constant<int, 16>{}, u, np, slot0, jp); break;
+    }
+  };
+
   // Phase 1 (not SPLIT): whole items below items_dp, one pipeline through all. Static order: items
   // xb, xb + G, ... With sp.queue, the dynamic order: the XCD's items in the same order (round r
   // of the static order gives XCD x items r G + x G/8 .. r G + x G/8 + G/8 - 1), but each
@@ -628,89 +742,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
       cu = nx;
       have_next = next(seq, nx);
     }
+
+    // Phase 2 (LAST_RANGES): the last round's items [items_dp, items), fewer than the grid, each
+    // cut along K into sp.parts ranges. A workgroup that has run out of whole items takes the next
+    // range from one counter, so the ranges go to the workgroups that finish first and the grid
+    // ends together instead of a few workgroups running a whole item more. Ranges are taken in
+    // counter order, so the ranges an item's parts wait for have been or will be taken by
+    // workgroups that are running.
+    if constexpr (LAST_RANGES) {
+      const int parts = sp.parts;
+      const int nranges = (items - items_dp) * parts;
+      int* const words = (int*)sp.ws;
+      for (;;) {
+        barrier();   // every wave is past its last LDS read, of the ring and of the slot
+        if (tid == 0) *slot = __hip_atomic_fetch_add(words + TAIL_CTR_WORD + zero, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        wait_lds_reads();
+        barrier();
+        const int r = __builtin_amdgcn_readfirstlane(*slot);
+        if (r >= nranges) break;
+        split_part(items_dp + r / parts, r % parts, parts, r / parts * parts, words + TAIL_FLAG_WORD0);
+      }
+    }
   }
 
   // Phase 2 (SPLIT, a launch of its own): the items [items_dp, items) (all of them; fewer than the
-  // grid). Each is cut along K into sp.parts equal ranges
-  // of blocks, run side by side by workgroups parts * t .. parts * t + parts - 1 (consecutive, so
-  // on one XCD). Every part writes its fp32 partial tile to its slot of the workspace and raises
-  // its flag; once all of the item's flags are up, part j sums share j (a 1/parts slice of the
-  // tile) over the item's partials and stores it to C. The flags were cleared on the stream
-  // before the launch. The grid is one workgroup per compute unit, and an item's parts are
-  // consecutive workgroups that start together, so the parts a workgroup waits for are running;
-  // should one ever not be, the wait ends after a bounded number of polls and sets the
-  // workspace's error word (the item's output is then wrong, and reported, rather than hung).
+  // grid). Each is cut along K into sp.parts ranges run side by side by workgroups parts * t ..
+  // parts * t + parts - 1 (consecutive, so on one XCD), flags in words 0 .. items * parts - 1 of
+  // the workspace, cleared on the stream before the launch. The grid is one workgroup per compute
+  // unit, and an item's parts are consecutive workgroups that start together, so the parts a
+  // workgroup waits for are running.
   if constexpr (SPLIT) {
     const int parts = sp.parts;
     const int t = xb / parts, jp = xb % parts;
     if (items_dp + t >= items) return;
-    const int L = items_dp + t;
-    const int kb0 = jp * KB / parts, kend = (jp + 1) * KB / parts;
-    int* flags = (int*)sp.ws;
-    const int slot = t * parts + jp;
-    const __amdgpu_buffer_rsrc_t pr =
-        make_rsrc(sp.ws + SPLIT_FLAG_BYTES + (size_t)slot * SPLIT_SLOT_BYTES, SPLIT_SLOT_BYTES);
-    Unit u[2];
-    const int np = __builtin_amdgcn_readfirstlane(item_units(p, tm, n_blocks, L, u));
-    for (int ps = 0; ps < np; ps++) {
-      Unit w = ps == 0 ? u[0] : u[1];
-      w.e = __builtin_amdgcn_readfirstlane(w.e);
-      w.row0 = __builtin_amdgcn_readfirstlane(w.row0);
-      w.rows = __builtin_amdgcn_readfirstlane(w.rows);
-      w.n0 = __builtin_amdgcn_readfirstlane(w.n0);
-      if (ps > 0) barrier();   // every wave is past its last LDS read of the previous pass
-      run_unit(w, kb0, kend, true, false, w, false, false);   // never piped, never HALF
-      // partial tile: per (wave, pass) 32 x 1 KiB, lane-contiguous; a pass of an item of two
-      // passes has at most 128 rows (waves 0-3), so its second pass uses waves 4-7's space
-      if (wm * WM < w.rows) {
-        const uint32_t pv = (uint32_t)(((wave + 4 * ps) * (MI * NJ * kWave) + lane) * 16);
-#pragma unroll
-        for (int i = 0; i < MI; i++)
-#pragma unroll
-          for (int j = 0; j < NJ; j++)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc[i][j]), pr, pv,
-                                                   (i * NJ + j) * kWave * 16, SC_AGENT);
-      }
-    }
-    wait_vmcnt<0>();   // this wave's partial has reached the agent's coherence point
-    barrier();
-    if (tid == 0) {
-      __hip_atomic_store(flags + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int m = 0; m < parts; m++) {
-        int spins = 0;
-        while (__hip_atomic_load(flags + t * parts + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-          if (++spins > SPLIT_SPIN_LIMIT) {   // never expected: give up, record it, go on
-            __hip_atomic_store(flags + SPLIT_ERR_WORD, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(8);
-        }
-      }
-    }
-    barrier();
-    // Share jp: v4f entries [jp * per, (jp + 1) * per) of the 8 x 32 x 64 in a tile; thread tid
-    // takes entries jp * per + k * 512 + tid. Entry g is lane g % 64 of fragment (g / 64) % 32 of
-    // wave slot g / 2048 (pass ws / 4 of a two-pass item, else pass 0), as the waves wrote them.
-    constexpr int ENTRIES = 8 * MI * NJ * kWave;
-    const int per = ENTRIES / parts;
-    const __amdgpu_buffer_rsrc_t all =
-        make_rsrc(sp.ws + SPLIT_FLAG_BYTES + (size_t)t * parts * SPLIT_SLOT_BYTES, (uint64_t)parts * SPLIT_SLOT_BYTES);
-    for (int k = 0; k < per / NTHREADS; k++) {
-      const int g = jp * per + k * NTHREADS + tid;
-      const int wsl = g / (MI * NJ * kWave), idx = (g / kWave) % (MI * NJ), ln = g % kWave;
-      const int ps = np == 2 ? wsl >> 2 : 0;
-      const int vw = np == 2 ? wsl & 3 : wsl;          // the wave that held the entry
-      Unit w = ps == 0 ? u[0] : u[1];
-      const int fi = idx / NJ, fj = idx % NJ;
-      const int mloc = (vw >> 1) * WM + fi * 16 + (ln & 15);
-      const int col = w.n0 + (vw & 1) * WN + ((fj >> 1) << 5) + ((ln >> 4) << 3) + ((fj & 1) << 2);
-      if (ps >= np || mloc >= w.rows || col >= N) continue;
-      v4f sum = (v4f){0.f, 0.f, 0.f, 0.f};
-      for (int m = 0; m < parts; m++)
-        sum += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                           all, (uint32_t)g * 16, (uint32_t)(m * SPLIT_SLOT_BYTES), SC_AGENT));
-      store4<OUT>(C, (size_t)(w.row0 + mloc) * N + col, sum[0], sum[1], sum[2], sum[3]);
-    }
+    split_part(items_dp + t, jp, parts, t * parts, (int*)sp.ws);
   }
 }
 
@@ -723,23 +789,14 @@ __global__ void zero_words_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-template <int OUT, bool SPLIT>
+template <int OUT, bool SPLIT, bool LAST_RANGES>
 hipError_t launch_out(const GemmArgs& a, int n_blocks, unsigned grid, SplitArgs sp, hipStream_t stream) {
-  const int32_t* eids = a.expert_ids;
-  const int32_t* toffs = a.tile_offsets;
-  void* c = a.C;
-  if constexpr (!SPLIT) {
-    hipLaunchKernelGGL((bw_fp8_grouped_kernel<OUT, false>), dim3(grid), dim3(NTHREADS), 0, stream, a, n_blocks,
-                       eids, toffs, c, sp);
-    return hipGetLastError();
-  } else {
-    hipLaunchKernelGGL((bw_fp8_grouped_kernel<OUT, true>), dim3(grid), dim3(NTHREADS), 0, stream, a, n_blocks,
-                       eids, toffs, c, sp);
-    return hipGetLastError();
-  }
+  hipLaunchKernelGGL((bw_fp8_grouped_kernel<OUT, SPLIT, LAST_RANGES>), dim3(grid), dim3(NTHREADS), 0, stream, a, n_blocks,
+                     a.expert_ids, a.tile_offsets, a.C, sp);
+  return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool LAST_RANGES = false>
 hipError_t launch(const GemmArgs& a0, int out, int n_blocks, unsigned grid, SplitArgs sp, hipStream_t stream) {
   GemmArgs a = a0;
   // Super-tiles per group of the work order (see the kernel): 8, so that an XCD's 32 items in
@@ -747,9 +804,9 @@ hipError_t launch(const GemmArgs& a0, int out, int n_blocks, unsigned grid, Spli
   // column blocks), which measured 10-15 % faster on the 8-expert N = 2048 workload.
   a.group_m = n_blocks <= 8 ? 1 : 8;
   switch (out) {
-    case kOutF32: return launch_out<kOutF32, SPLIT>(a, n_blocks, grid, sp, stream);
-    case kOutBF16: return launch_out<kOutBF16, SPLIT>(a, n_blocks, grid, sp, stream);
-    case kOutF16: return launch_out<kOutF16, SPLIT>(a, n_blocks, grid, sp, stream);
+    case kOutF32: return launch_out<kOutF32, SPLIT, LAST_RANGES>(a, n_blocks, grid, sp, stream);
+    case kOutBF16: return launch_out<kOutBF16, SPLIT, LAST_RANGES>(a, n_blocks, grid, sp, stream);
+    case kOutF16: return launch_out<kOutF16, SPLIT, LAST_RANGES>(a, n_blocks, grid, sp, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -783,10 +840,7 @@ hipError_t launch_blockwise_fp8_split(const GemmArgs& a, int out, void* ws, size
   if (items == 0) return hipSuccess;
   if (items > 0x7ffffff0LL) return hipErrorInvalidValue;
   // With fewer items than workgroups, each item is cut along K into `parts` ranges (a power of
-  // 2, at most 16, each at least 8 K blocks), as many as the grid holds. With whole rounds of
-  // items the split is not used: cutting only the last round's items measured no faster than
-  // running them whole (the partial tiles' traffic and the second launch cost what the idle
-  // workgroups lose).
+  // 2, at most 16, each at least 8 K blocks), as many as the grid holds.
   // A workspace smaller than blockwise_fp8_workspace_bytes (at least the flags) holds fewer
   // partial tiles; the split then uses fewer ranges, so that every range has its tile.
   if (ws == nullptr || ws_bytes < SPLIT_FLAG_BYTES) return hipErrorInvalidValue;
@@ -794,19 +848,33 @@ hipError_t launch_blockwise_fp8_split(const GemmArgs& a, int out, void* ws, size
   const long long tail = items < (long long)G ? items : 0;
   int parts = 1;
   while (tail > 0 && parts < 16 && 2 * parts * 8 <= KB && tail * 2 * parts <= slots) parts *= 2;
+  const int words = (int)(SPLIT_FLAG_BYTES / 4);
   if (parts < 2 || G > SPLIT_FLAG_BYTES / 4 - 1) {
-    // Whole items. With at least a round of items of DYNAMIC_MIN_KB or more K blocks, the dynamic
-    // work order with 8 counters in the workspace. Measured on the 32-expert workload in one job:
-    // gate_up (56 K blocks) 3.48 -> 3.33 ms, while down (16 K blocks, whose workgroups change
-    // items more often, so that the XCD's items in flight straddle two rounds' runs more often)
-    // went 1.81 -> 1.88 ms and the 8-expert one (32 K blocks) did not change.
-    if (items < (long long)G || KB < DYNAMIC_MIN_KB) return launch_blockwise_fp8(a, out, stream);
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, (int*)ws, 8);
+    if (items < (long long)G) return launch_blockwise_fp8(a, out, stream);
+    // Whole items, in one launch with two additions that need the workspace:
+    // * items of DYNAMIC_MIN_KB or more K blocks take the dynamic work order (8 counters).
+    //   Measured on the 32-expert workload in one job: gate_up (56 K blocks) 3.48 -> 3.33 ms,
+    //   while down (16 K blocks, whose workgroups change items more often, so that the XCD's
+    //   items in flight straddle two rounds' runs more often) went 1.81 -> 1.88 ms and the
+    //   8-expert one (32 K blocks) did not change;
+    // * in a launch of fewer than TAIL_MAX_ROUNDS rounds, the last round's items (items % G of
+    //   them) are cut along K into tparts ranges (a power of 2, at most 16, each at least
+    //   TAIL_MIN_KB blocks, as many as the grid and the workspace hold) that the workgroups which
+    //   run out of whole items first take from a counter.
+    const bool dyn = KB >= DYNAMIC_MIN_KB;
+    const long long last = items % G;
+    int tparts = 1;
+    while (last > 0 && items < (long long)TAIL_MAX_ROUNDS * G && tparts < 16 && KB >= 2 * tparts * TAIL_MIN_KB &&
+           last * 2 * tparts <= slots && TAIL_FLAG_WORD0 + last * 2 * tparts < SPLIT_ERR_WORD)
+      tparts *= 2;
+    if (!dyn && tparts < 2) return launch_blockwise_fp8(a, out, stream);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream, (int*)ws, words);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch<false>(a, out, n_blocks, grid_for(a.num_cus), SplitArgs{(int)items, 1, nullptr, (int*)ws}, stream);
+    if (tparts < 2) return launch<false>(a, out, n_blocks, G, SplitArgs{(int)items, 1, nullptr, (int*)ws}, stream);
+    return launch<false, true>(a, out, n_blocks, G,
+                               SplitArgs{(int)(items - last), tparts, (uint8_t*)ws, dyn ? (int*)ws : nullptr}, stream);
   }
-  const int words = (int)(SPLIT_FLAG_BYTES / 4);
   hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream, (int*)ws, words);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

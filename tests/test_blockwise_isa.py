@@ -48,6 +48,14 @@ def test_whole_item_kernels_do_not_spill(asm):
     names = re.findall(r"\.name:\s+(\S+)", text)
     spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
     assert len(names) == len(spills)
+    forms = 0
     for n, v in zip(names, spills):
-        if "Lb0E" in n:   # bw_fp8_grouped_kernel<OUT, false>
+        # bw_fp8_grouped_kernel<OUT, false, false>: every launch of whole items of at least four
+        # rounds. The form with the last round's ranges (<OUT, false, true>, shorter launches) may
+        # keep a few values in scratch across a unit's start.
+        if "Lb0ELb0E" in n:
+            forms += 1
             assert int(v) == 0, n
+        elif "Lb0ELb1E" in n:
+            assert int(v) <= 4, n
+    assert forms == 3

@@ -55,6 +55,49 @@ def split_parts(tiles, N, K):
     return parts
 
 
+def tail_parts(tiles, N, K, slots=None):
+    """Ranges per item of the last round's items in a whole-items launch through the workspace
+    (the library's rule; 1: none)."""
+    G = num_cus() // 8 * 8
+    items, KB = items_of(tiles, N), K // 128
+    if items < G or items >= 4 * G:
+        return 1
+    slots = G if slots is None else min(G, slots)
+    last, t = items % G, 1
+    while last > 0 and t < 16 and KB >= 2 * t * 4 and last * 2 * t <= slots and 16 + last * 2 * t < ERR_WORD:
+        t *= 2
+    return t
+
+
+def item_cell(L, tiles, N):
+    """(super-tile, first column) of work item L in the kernel's order: groups of group_m
+    super-tiles (1 with at most 8 column blocks, else 8) walk their column blocks together."""
+    n_blocks = -(-N // 256)
+    group_m = 1 if n_blocks <= 8 else 8
+    gsz = group_m * n_blocks
+    g0 = (L // gsz) * group_m
+    gm = min(group_m, (tiles + 1) // 2 - g0)
+    r = L % gsz
+    return g0 + r % gm, (r // gm) * 256
+
+
+def tail_mask(p, tile_offsets=None):
+    """Boolean [M, N] over the cells of the last round's items (rows of both tiles of the
+    super-tile, by tile_offsets; padded layout when None)."""
+    T = p.M // 128
+    G = num_cus() // 8 * 8
+    items = items_of(T, p.N)
+    to = np.arange(T + 1) * 128 if tile_offsets is None else tile_offsets.cpu().numpy()
+    mask = np.zeros((p.M, p.N), bool)
+    for L in range(items - items % G, items):
+        s, n0 = item_cell(L, T, p.N)
+        for t in (2 * s, 2 * s + 1):
+            if t < T:
+                r0 = int(to[t])
+                mask[r0:r0 + min(128, int(to[t + 1]) - r0), n0:n0 + 256] = True
+    return torch.from_numpy(mask).cuda()
+
+
 def run_ws(p, out, ws, tile_map=None):
     C = poisoned(p.M, p.N, out)
     ei = to = None
@@ -166,21 +209,72 @@ def test_dynamic_work_order_dense_bit_identical(workspace):
 def test_dynamic_work_order_grouped_with_skipped_items(workspace):
     """Ragged groups of 40 experts at K = 5120 with every fourth super-tile's tiles given an
     out-of-range expert id: items without a live tile are taken and passed over (the counter is
-    asked again), their rows stay untouched, and everything matches bsgemm_grouped bit for bit."""
+    asked again), their rows stay untouched. Outside the last round's items (cut along K into
+    ranges, whose partial sums round differently) everything matches bsgemm_grouped bit for bit;
+    two calls give the same bits."""
     rng = np.random.default_rng(11)
     counts = rng.integers(0, 4000, 40)
     counts[[2, 9]] = 0
     p = blockwise_problem([int(c) for c in counts], 256, 5120, device="cuda", seed=52)
     T = p.M // 128
     assert _dyn_applies(T, p.N, p.K)
+    say(f"[dyn] items={items_of(T, p.N)} last-round ranges per item={tail_parts(T, p.N, p.K)}")
     _, to, ei = gpu_tile_map(p.counts, T)
     ei = ei.clone()
     ei.view(-1)[0::8] = 1000     # both tiles of every fourth super-tile: expert out of range
     ei.view(-1)[1::8] = -1
     C_static, outs = _static_and_ws(p, ei, to, "bf16", workspace)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    mask = tail_mask(p, to) if tail_parts(T, p.N, p.K) > 1 else torch.zeros_like(C_static, dtype=torch.bool)
     for C in outs:
-        assert torch.equal(C.view(torch.int16), C_static.view(torch.int16))
+        assert torch.equal(C.view(torch.int16)[~mask], C_static.view(torch.int16)[~mask])
     ei_h = ei.cpu().numpy().copy()
     ei_h[(ei_h < 0) | (ei_h >= p.E)] = -1
     check(p, "bf16", outs[-1], rows=sample_rows(p), tile_map_ref=(ei_h, to.cpu().numpy()),
           label="dynamic order with skipped items")
+
+
+@pytest.mark.parametrize("M,N,K,out", [
+    (8448, 2048, 4096, "bf16"),   # 264 items: 256 whole (static order), the last 8 in 8 ranges of 4
+    (8704, 4096, 5120, "f32"),    # 544 items: dynamic order, the last 32 in 8 ranges of 5 blocks
+    (16640, 2048, 4096, "f16"),   # 520 items: static order, the last 8 in 8 ranges of 4 blocks
+])
+def test_last_round_split_dense(workspace, M, N, K, out):
+    """The last round's items, fewer than the grid, are cut along K and taken by the workgroups
+    that finish first: the oracle on every row of those items and sampled rows elsewhere, the
+    rest bit-identical to bsgemm_grouped, two calls bit-identical."""
+    T = M // 128
+    parts = tail_parts(T, N, K)
+    say(f"[tail] items={items_of(T, N)} ranges per item={parts}")
+    assert parts >= 2
+    p = blockwise_problem(None, N, K, device="cuda", a_rows=M, seed=M + N)
+    C_static, outs = _static_and_ws(p, None, None, out, workspace)
+    assert int(workspace[: 4 * (ERR_WORD + 1)].view(torch.int32)[ERR_WORD]) == 0
+    bits = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits))
+    mask = tail_mask(p)
+    assert bool(mask.any())
+    assert torch.equal(outs[0].view(bits)[~mask], C_static.view(bits)[~mask])
+    tail_rows = np.nonzero(mask.any(dim=1).cpu().numpy())[0]
+    rows = np.union1d(sample_rows(p, per_tile=10), tail_rows)
+    check(p, out, outs[0], rows=rows, label=f"last-round split {M}x{N}x{K}")
+
+
+def test_last_round_split_moe8(workspace):
+    """The 8-expert workload (272 items, the last 16 in 8 ranges; tiles of two experts share
+    super-tiles): oracle on sampled rows of every tile and on all rows of the last round's items."""
+    from workloads.generate import make_problem
+    p = make_problem("moe8_n2048_k4096", device="cuda", seed=0)
+    T = p.M // 128
+    parts = tail_parts(T, p.N, p.K)
+    say(f"[tail] items={items_of(T, p.N)} ranges per item={parts}")
+    assert parts >= 2
+    _, to, ei = gpu_tile_map(p.counts, T)
+    C_static, outs = _static_and_ws(p, ei, to, "bf16", workspace)
+    assert int(workspace[: 4 * (ERR_WORD + 1)].view(torch.int32)[ERR_WORD]) == 0
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    mask = tail_mask(p, to)
+    assert torch.equal(outs[0].view(torch.int16)[~mask], C_static.view(torch.int16)[~mask])
+    tail_rows = np.nonzero(mask.any(dim=1).cpu().numpy())[0]
+    rows = np.union1d(sample_rows(p, per_tile=4), tail_rows)
+    check(p, "bf16", outs[0], rows=rows, label="last-round split moe8")

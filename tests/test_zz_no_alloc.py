@@ -64,3 +64,24 @@ def test_noalloc_dynamic_work_order_bit_identical():
         torch.cuda.synchronize()
         assert torch.equal(C.view(torch.int16), C_ref.view(torch.int16)), f"call {call}"
         say(f"[no-alloc] dynamic order call {call}: bit-identical")
+
+
+def test_noalloc_last_round_split_matches_workspace_call():
+    """8448 x 2048 x 4096 (264 items): the last 8 items are cut into 8 K ranges whose partial tiles
+    fit the library's scratch as they fit a full workspace, so the no-alloc call equals the
+    workspace call bit for bit, twice in a row, and bsgemm_grouped outside those items."""
+    p = blockwise_problem(None, 2048, 4096, device="cuda", a_rows=8448, seed=62)
+    fmt = bsg.make_fmt("e4m3", "e4m3", "blockwise", "bf16")
+    ws = torch.empty(bsg.bsgemm_grouped_workspace_size(), dtype=torch.uint8, device="cuda")
+    C_ws = poisoned(p.M, p.N, "bf16")
+    bsg.bsgemm_grouped_ws(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C_ws, p.M, p.N, p.K, fmt, ws)
+    C_ref = poisoned(p.M, p.N, "bf16")
+    bsg.bsgemm_grouped(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C_ref, p.M, p.N, p.K, fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(C_ws[:8192].view(torch.int16), C_ref[:8192].view(torch.int16))
+    for call in (1, 2):
+        C = poisoned(p.M, p.N, "bf16")
+        bsg.bsgemm_grouped_noalloc(p.qa, p.a_scales, p.qb, p.b_scales, None, None, C, p.M, p.N, p.K, fmt)
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int16), C_ws.view(torch.int16)), f"call {call}"
+    check(p, "bf16", C, rows=np.arange(8192, 8448), label="no-alloc last-round split")
