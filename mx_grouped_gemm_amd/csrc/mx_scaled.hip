@@ -249,15 +249,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
   int cbase = 0;
   v4f acc[MI][NJ];
 
-  // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, moved to byte 0
+  // lane (r16, q) supplies the scale of chunk q: byte q of the row's dword, read as a byte (one LDS
+  // read and no shift; measured 1.5 % faster for e4m3 x e4m3 and 5 % for e4m3 x e2m1 than a dword
+  // read and a shift)
   // g: 128-K sub-block index of the unit (stage b holds sub-blocks KS b .. KS b + KS - 1)
   auto scale_a = [&](int g, int i) {
     const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
-    return (int)(*(const uint32_t*)(smem + base_sa + so + i * 16 * SC_CHUNK * 4) >> (8 * q));
+    return (int)*(const uint8_t*)(smem + base_sa + q + so + i * 16 * SC_CHUNK * 4);
   };
   auto scale_b = [&](int g, int j) {
     const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
-    return (int)(*(const uint32_t*)(smem + base_sb + so + j * 16 * SC_CHUNK * 4) >> (8 * q));
+    return (int)*(const uint8_t*)(smem + base_sb + q + so + j * 16 * SC_CHUNK * 4);
   };
 
   // The stages of unit u into acc. prologue: copy the unit's first stages and scale chunks and
