@@ -139,25 +139,70 @@ __device__ __forceinline__ void mx_copy_b(uint32_t dst, const MxLoadPlan<FA, FB,
   buf2lds16(lp.b_rsrc, lp.b_voff[i], (uint32_t)__builtin_amdgcn_readfirstlane(kb) * L::RB, lds_ptr(dst + i * 1024));
 }
 
-// Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows into
-// [row][8 dwords] layouts; wave w copies rows 32 w .. 32 w + 31 of each (instruction i: rows
-// 32 w + 8 i + lane / 8, dword lane % 8; LDS row r of the B half holds B row (r & 128) |
-// b_col(r & 127), as the B tile does). The per-lane offsets are formed here, once per chunk (an
-// empty asm keeps the compiler from keeping them live across the K loop).
-template <int FA, int FB, int KS>
+// Scale chunk c (K blocks 8c .. 8c+7) of the super-tile's 256 A rows and 256 B rows, one dword
+// (the four 32-K chunks of a K block) per row and K block. LDS row r of the B half holds B row
+// (r & 128) | b_col(r & 127), as the B tile does. Two layouts:
+// * by row (PK false): [row][8 dwords]; wave w copies rows 32 w .. 32 w + 31 of each
+//   (instruction i: rows 32 w + 8 i + lane / 8, dword lane % 8);
+// * packed (PK true): the dwords a lane's fragments need side by side, so that one 16-byte read
+//   gives a K block's dwords of 4 fragments. A: [64-row group][r16][K block slot][fragment f] for
+//   row 64 g + 16 f + r16; B: [128-row group][r16][K block slot][fragment j] for LDS row
+//   128 g + 16 j + r16. K block k of row group (g, r16) sits in slot k ^ (r16 & 7), so that the
+//   16 lanes of different r16 that read one K block hit different banks.
+// The per-lane offsets are formed here, once per chunk (an empty asm keeps the compiler from
+// keeping them live across the K loop).
+template <int FA, int FB, int KS, bool PK>
 __device__ __forceinline__ void mx_issue_scales(uint32_t dsa, uint32_t dsb, const MxLoadPlan<FA, FB, KS>& lp,
                                                 int chunk, int wave) {
   const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * SC_CHUNK * 4;
   int ln = (int)(threadIdx.x & 63);
   asm volatile("" : "+v"(ln));
-  const int lrow = ln >> 3, dw = ln & 7;
 #pragma unroll
   for (int i = 0; i < SC_INSTR; i++) {
-    const int r = wave * 32 + 8 * i + lrow;
-    const uint32_t va = (uint32_t)r * lp.srow + dw * 4 + col;
-    const uint32_t vb = (uint32_t)((r & 128) | b_col(r & 127)) * lp.srow + dw * 4 + col;
+    uint32_t va, vb;
+    if constexpr (PK) {
+      const int p = (wave * SC_INSTR + i) * 64 + ln;   // dword of the chunk this lane writes
+      const int fa = p & 3, sa = (p >> 2) & 7, ra = (p >> 5) & 15, ga = p >> 9;
+      va = (uint32_t)(ga * 64 + fa * 16 + ra) * lp.srow + (sa ^ (ra & 7)) * 4 + col;
+      const int jb = p & 7, sb = (p >> 3) & 7, rb = (p >> 6) & 15, gb = p >> 10;
+      const int lr = gb * 128 + jb * 16 + rb;
+      vb = (uint32_t)((lr & 128) | b_col(lr & 127)) * lp.srow + (sb ^ (rb & 7)) * 4 + col;
+    } else {
+      const int r = wave * 32 + 8 * i + (ln >> 3), dw = ln & 7;
+      va = (uint32_t)r * lp.srow + dw * 4 + col;
+      vb = (uint32_t)((r & 128) | b_col(r & 127)) * lp.srow + dw * 4 + col;
+    }
     buf2lds4(lp.sa_rsrc, va, 0, lds_ptr(dsa + i * 256));
     buf2lds4(lp.sb_rsrc, vb, 0, lds_ptr(dsb + i * 256));
+  }
+}
+
+// The scaled MFMA taking byte JS of sb and byte IS of sa as the lane's scales.
+template <int FA, int FB, int JS, int IS>
+__device__ __forceinline__ v4f mma_sel(const v8i& b, const v8i& a, const v4f& c, int sb, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, Elem<FB>::kCode, Elem<FA>::kCode,
+                                                          JS, sb, IS, sa);
+}
+// jsel, isel in 0..3, constants once the pass loops are unrolled (the switch then folds away)
+template <int FA, int FB>
+__device__ __forceinline__ v4f mma_p(const v8i& b, const v8i& a, const v4f& c, int sb, int jsel, int sa, int isel) {
+  switch (jsel * 4 + isel) {
+    case 0: return mma_sel<FA, FB, 0, 0>(b, a, c, sb, sa);
+    case 1: return mma_sel<FA, FB, 0, 1>(b, a, c, sb, sa);
+    case 2: return mma_sel<FA, FB, 0, 2>(b, a, c, sb, sa);
+    case 3: return mma_sel<FA, FB, 0, 3>(b, a, c, sb, sa);
+    case 4: return mma_sel<FA, FB, 1, 0>(b, a, c, sb, sa);
+    case 5: return mma_sel<FA, FB, 1, 1>(b, a, c, sb, sa);
+    case 6: return mma_sel<FA, FB, 1, 2>(b, a, c, sb, sa);
+    case 7: return mma_sel<FA, FB, 1, 3>(b, a, c, sb, sa);
+    case 8: return mma_sel<FA, FB, 2, 0>(b, a, c, sb, sa);
+    case 9: return mma_sel<FA, FB, 2, 1>(b, a, c, sb, sa);
+    case 10: return mma_sel<FA, FB, 2, 2>(b, a, c, sb, sa);
+    case 11: return mma_sel<FA, FB, 2, 3>(b, a, c, sb, sa);
+    case 12: return mma_sel<FA, FB, 3, 0>(b, a, c, sb, sa);
+    case 13: return mma_sel<FA, FB, 3, 1>(b, a, c, sb, sa);
+    case 14: return mma_sel<FA, FB, 3, 2>(b, a, c, sb, sa);
+    default: return mma_sel<FA, FB, 3, 3>(b, a, c, sb, sa);
   }
 }
 
@@ -208,8 +253,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
 
   const FragBase<L::RA> fa = frag_base<L::RA>(wm * WM + r16, r16, q);
   const FragBase<L::RB> fb = frag_base<L::RB>(wn * WN + r16, r16, q);
-  const int base_sa = L::SA_REGION + (wm * WM + r16) * SC_CHUNK * 4;
-  const int base_sb = L::SB_REGION + (wn * WN + r16) * SC_CHUNK * 4;
+  // Scale layout (see mx_issue_scales): packed for A and B of one format, by row for a mixed
+  // pair. Measured at 8192^3 against reading each scale as a byte: e2m1 x e2m1 0.321 -> 0.295 ms,
+  // e4m3 x e4m3 0.498 -> 0.489 ms, e4m3 x e2m1 0.449 -> 0.460 ms (slower: by row there).
+  constexpr bool PK = FA == FB;
+  const int base_sa = PK ? L::SA_REGION + (wm * 16 + r16) * 128 : L::SA_REGION + (wm * WM + r16) * SC_CHUNK * 4;
+  const int base_sb = PK ? L::SB_REGION + (wn * 16 + r16) * 256 : L::SB_REGION + (wn * WN + r16) * SC_CHUNK * 4;
+  const int slot_x = r16 & 7;
+  // v_perm selector: byte q of the low source to byte 0, byte q of the high source to byte 1
+  const int sel01 = q | ((4 + q) << 8) | (0x0c << 16) | (0x0c << 24);
 
   // Copy plan. The per-lane offsets depend only on the lane, the wave and K; the resources
   // describe the unit being copied (rows past it or past N read as zero) and switch from one unit
@@ -261,6 +313,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
     const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (g % SC_CHUNK) * 4;
     return (int)*(const uint8_t*)(smem + base_sb + q + so + j * 16 * SC_CHUNK * 4);
   };
+  // Packed layout: sub-block g's dwords of the lane's 4 A fragments, or of B fragments 4 h ..
+  // 4 h + 3, in one read; pack4 keeps byte q of each (the lane's chunk), fragment f in byte f,
+  // which the MFMA then selects.
+  auto raw_a = [&](int g) {
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_x) * 16);
+    return lds_read16(smem + base_sa + so);
+  };
+  auto raw_b = [&](int g, int h) {
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_x) * 32) + h * 16;
+    return lds_read16(smem + base_sb + so);
+  };
+  auto pack4 = [&](const v4i d) {
+    const uint32_t x01 = __builtin_amdgcn_perm((uint32_t)d[1], (uint32_t)d[0], (uint32_t)sel01);
+    const uint32_t x23 = __builtin_amdgcn_perm((uint32_t)d[3], (uint32_t)d[2], (uint32_t)sel01);
+    return (int)__builtin_amdgcn_perm(x23, x01, 0x05040100u);
+  };
 
   // The stages of unit u into acc. prologue: copy the unit's first stages and scale chunks and
   // wait for them (else the previous unit's last stages copied them). pipe: the last two stages
@@ -280,8 +348,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       // scale chunks 0 and 1, stage 0 and the B half of stage 1 (its A half goes out in passes 0
       // and 1 of stage 0, as in every stage); stage 0 published
       const LdsBases lb = lds_bases<FA, FB, KS>(smem, wave);
-      mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION, lb.ws + L::SB_REGION, lp, 0, wave);
-      mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + SC_BYTES, lb.ws + L::SB_REGION + SC_BYTES, lp, 1, wave);
+      mx_issue_scales<FA, FB, KS, PK>(lb.ws + L::SA_REGION, lb.ws + L::SB_REGION, lp, 0, wave);
+      mx_issue_scales<FA, FB, KS, PK>(lb.ws + L::SA_REGION + SC_BYTES, lb.ws + L::SB_REGION + SC_BYTES, lp, 1, wave);
 #pragma unroll
       for (int i = 0; i < L::A_INSTR; i++) mx_copy_a<FA, FB, KS>(lb.wa + L::A_REGION, lp, 0, i);
 #pragma unroll
@@ -296,20 +364,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
     // A fragments and scales of the stage stay in registers; B fragments and their scales
     // stream through 3-deep queues two fragments ahead
     v8i af[MI], bq[3];
-    int sa[MI][KS], sbq[3][KS];
+    int sa[MI][KS], sbq[3][KS];     // by row: each fragment's scale in byte 0
+    int sa_p[KS], sb_p[KS][2];      // packed: fragment i (A) / j (B) in byte i / j % 4
 #pragma unroll
     for (int i = 0; i < MI; i++) {
       af[i] = read_frag<L::RA>(smem + L::A_REGION + i * 16 * L::RA, fa);
+      if constexpr (!PK) {
 #pragma unroll
-      for (int h = 0; h < KS; h++) sa[i][h] = scale_a(h, i);
+        for (int h = 0; h < KS; h++) sa[i][h] = scale_a(h, i);
+      }
     }
     bq[0] = read_frag<L::RB>(smem + L::B_REGION, fb);
     bq[1] = read_frag<L::RB>(smem + L::B_REGION + 16 * L::RB, fb);
 #pragma unroll
     for (int h = 0; h < KS; h++) {
-      sbq[0][h] = scale_b(h, 0);
-      sbq[1][h] = scale_b(h, 1);
+      if constexpr (PK) {
+        sa_p[h] = pack4(raw_a(h));
+        sb_p[h][0] = pack4(raw_b(h, 0));
+        sb_p[h][1] = pack4(raw_b(h, 1));
+      } else {
+        sbq[0][h] = scale_b(h, 0);
+        sbq[1][h] = scale_b(h, 1);
+      }
     }
+    // the MFMA of A fragment i, B fragment j, sub-block h with its scales
+    auto mma_ij = [&](const v8i& bop, const v8i& aop, const v4f& c, const int i, const int j, const int h) {
+      if constexpr (PK) return mma_p<FA, FB>(bop, aop, c, sb_p[h][j / 4], j % 4, sa_p[h], i);
+      else return mma<FA, FB>(bop, aop, c, sbq[j % 3][h], sa[i][h]);
+    };
 
     // copies per wave and pass: the A half of a stage over passes 0 and 1, the B half over
     // passes 6 and 7, each after the second or fourth MFMA of the pass
@@ -356,7 +438,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         for (int h = 0; h < KS; h++)
 #pragma unroll
         for (int i = 0; i < MI; i++) {
-          acc[i][j] = mma<FA, FB>(sub_op<KS>(bq[j % 3], h), sub_op<KS>(af[i], h), acc[i][j], sbq[j % 3][h], sa[i][h]);
+          acc[i][j] = mma_ij(sub_op<KS>(bq[j % 3], h), sub_op<KS>(af[i], h), acc[i][j], i, j, h);
           if (h < KS - 1) {
             __builtin_amdgcn_sched_barrier(0);
             continue;
@@ -366,8 +448,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
           if (j + 2 < NJ && i == 0) lo = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[0]);
           if (j + 2 < NJ && i == 2) {
             if constexpr (L::RB == 128) hi = lds_read16(smem + L::B_REGION + sob + (j + 2) * 16 * L::RB + fb.off[1]);
+            if constexpr (!PK) {
 #pragma unroll
-            for (int h = 0; h < KS; h++) sbn[h] = scale_b(KS * b + h, j + 2);
+              for (int h = 0; h < KS; h++) sbn[h] = scale_b(KS * b + h, j + 2);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -375,8 +459,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
         if (j + 2 < NJ) {
           if constexpr (L::RB == 128) bq[(j + 2) % 3] = cat(lo, hi);
           else bq[(j + 2) % 3] = (v8i){lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+          if constexpr (!PK) {
 #pragma unroll
-          for (int h = 0; h < KS; h++) sbq[(j + 2) % 3][h] = sbn[h];
+            for (int h = 0; h < KS; h++) sbq[(j + 2) % 3][h] = sbn[h];
+          }
         }
         // pin the previous pass's MFMAs (complete by now) ahead of this point, so that the
         // compiler does not sink them past the loop's branch
@@ -401,30 +487,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       if constexpr (!TAIL) {
         if (b % SCS == 0 && b > 0 && b / SCS + 1 < nchunks) {
           const int c = b / SCS + 1, cb = ((cbase + c) & 1) * SC_BYTES;
-          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, c, wave);
+          mx_issue_scales<FA, FB, KS, PK>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, c, wave);
         }
       }
       if constexpr (TAIL) {
         if (pipe && b == KB - 2) {
           rsrc_scales(nx, nx_live);
           const int cb = ((cbase + nchunks) & 1) * SC_BYTES;
-          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 0, wave);
+          mx_issue_scales<FA, FB, KS, PK>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 0, wave);
         }
         if (pipe && b == KB - 1) {
           const int cb = ((cbase + nchunks - 1) & 1) * SC_BYTES;
-          mx_issue_scales<FA, FB, KS>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 1, wave);
+          mx_issue_scales<FA, FB, KS, PK>(lb.ws + L::SA_REGION + cb, lb.ws + L::SB_REGION + cb, lp, 1, wave);
         }
       }
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 3]));
       __builtin_amdgcn_sched_barrier(0);
+      // packed: the next stage's scale dwords, packed at the end of pass 7 (after this stage's
+      // last MFMA that uses the current ones)
+      v4i ra_n[KS], rb_n[KS][2];
+      if constexpr (PK) {
+#pragma unroll
+        for (int h = 0; h < KS; h++) {
+          ra_n[h] = raw_a(KS * bn + h);
+          rb_n[h][0] = raw_b(KS * bn + h, 0);
+          rb_n[h][1] = raw_b(KS * bn + h, 1);
+        }
+      }
       // pass 6 with the first copies of the B half of stage b+2 into stage S
 #pragma unroll
       for (int h = 0; h < KS; h++)
 #pragma unroll
       for (int i = 0; i < MI; i++) {
-        acc[i][NJ - 2] = mma<FA, FB>(sub_op<KS>(bq[(NJ - 2) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 2],
-                                     sbq[(NJ - 2) % 3][h], sa[i][h]);
+        acc[i][NJ - 2] = mma_ij(sub_op<KS>(bq[(NJ - 2) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 2], i, NJ - 2, h);
         if ((i & 1) && (i >> 1) < B_PP && h == KS - 1)
           mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION + sob, lp, kb_b, i >> 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -437,15 +533,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       for (int h = 0; h < KS; h++)
 #pragma unroll
       for (int i = 0; i < MI; i++) {
-        acc[i][NJ - 1] = mma<FA, FB>(sub_op<KS>(bq[(NJ - 1) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 1],
-                                     sbq[(NJ - 1) % 3][h], sa[i][h]);
+        acc[i][NJ - 1] = mma_ij(sub_op<KS>(bq[(NJ - 1) % 3], h), sub_op<KS>(af[i], h), acc[i][NJ - 1], i, NJ - 1, h);
         if (h < KS - 1) {
           __builtin_amdgcn_sched_barrier(0);
           continue;
         }
         af[i] = read_frag<L::RA>(smem + L::A_REGION + sna + i * 16 * L::RA, fa);
+        if constexpr (!PK) {
 #pragma unroll
-        for (int h = 0; h < KS; h++) sa[i][h] = scale_a(KS * bn + h, i);
+          for (int h = 0; h < KS; h++) sa[i][h] = scale_a(KS * bn + h, i);
+        }
         if ((i & 1) && (i >> 1) < B_PP)
           mx_copy_b<FA, FB, KS>(lb.wb + L::B_REGION + sob, lp, kb_b, B_PP + (i >> 1));
         __builtin_amdgcn_sched_barrier(0);
@@ -454,8 +551,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
       bq[1] = read_frag<L::RB>(smem + L::B_REGION + snb + 16 * L::RB, fb);
 #pragma unroll
       for (int h = 0; h < KS; h++) {
-        sbq[0][h] = scale_b(KS * bn + h, 0);
-        sbq[1][h] = scale_b(KS * bn + h, 1);
+        if constexpr (PK) {
+          sa_p[h] = pack4(ra_n[h]);
+          sb_p[h][0] = pack4(rb_n[h][0]);
+          sb_p[h][1] = pack4(rb_n[h][1]);
+        } else {
+          sbq[0][h] = scale_b(KS * bn + h, 0);
+          sbq[1][h] = scale_b(KS * bn + h, 1);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MI; i++) asm volatile("" : "+v"(acc[i][NJ - 2]));
