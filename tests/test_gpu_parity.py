@@ -304,6 +304,16 @@ def test_mx_e2m1_k_depths(K):
     check(p, "f32", C, label=f"mx e2m1xe2m1 K={K}")
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e4m3", "e2m1")])
+def test_mx_ragged_rows_and_columns(fa, fb):
+    """M = 200 and N = 384: the super-tile's last 56 rows and the second column block's last 128
+    columns lie past the operands, so their staged scales (packed for a pair of one format) are
+    zeros that no stored output uses; K = 2304 spans two scale chunks and a partial third."""
+    p = mx_problem(200, 384, 2304, fa, fb, device="cuda", seed=23)
+    C, _, _ = run_problem(p, "f32")
+    check(p, "f32", C, label=f"mx ragged {fa}x{fb}")
+
+
 @pytest.mark.parametrize("fa,fb", MX_PAIRS)
 def test_mx_exact_products_bit_exact(fa, fb):
     """Layout pin for elements, nibble order and per-32 scales: small values and scales near 1
