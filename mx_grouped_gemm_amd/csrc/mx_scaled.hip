@@ -59,11 +59,19 @@ struct Layout {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// 16-byte chunk swizzle of a tile row: 128-byte rows (e4m3) use swz8; for 64-byte rows (e2m1)
-// two rows share a 128-byte bank line, and rows of one parity take the four slot permutations.
+// 16-byte chunk swizzle of a tile row: chunk c of LDS row r sits at slot c ^ swzr(r). The LDS
+// serves a 16-byte read 32 lanes at a time across 512 bytes of banks (128 x 4), so the 32 lanes
+// (r16 = 0..15, two values of q) of one read must hit 32 different 16-byte bank slots. A lane
+// reads chunk q (and 4 + q) of row r16 of a fragment: with 128-byte rows the slot is 8 (r16 & 3) +
+// (c ^ swzr), so the four rows of one r16 & 3 need swzr values of distinct halves (bits 1-2 from
+// r16 >> 2); with 64-byte rows it is 4 (r16 & 7) + (c ^ swzr), so rows r16 and r16 + 8 need
+// different swzr. (The blockwise kernel's swizzle, swz8, left every fragment read two-way
+// conflicted here, where each lane reads chunks q and 4 + q rather than 2 q and 2 q + 1: the
+// LDS bank-conflict stall cycles equalled its busy cycles.)
 template <int ROWB>
 __device__ __forceinline__ int swzr(int r) {
-  if constexpr (ROWB == 128) return swz8(r); else return (r >> 1) & 3;
+  if constexpr (ROWB == 128) return (((r >> 2) & 3) << 1) | ((r >> 1) & 1);
+  else return (r >> 2) & 3;
 }
 
 template <int ROWB>
@@ -147,8 +155,9 @@ __device__ __forceinline__ void mx_copy_b(uint32_t dst, const MxLoadPlan<FA, FB,
 // * packed (PK true): the dwords a lane's fragments need side by side, so that one 16-byte read
 //   gives a K block's dwords of 4 fragments. A: [64-row group][r16][K block slot][fragment f] for
 //   row 64 g + 16 f + r16; B: [128-row group][r16][K block slot][fragment j] for LDS row
-//   128 g + 16 j + r16. K block k of row group (g, r16) sits in slot k ^ (r16 & 7), so that the
-//   16 lanes of different r16 that read one K block hit different banks.
+//   128 g + 16 j + r16. K block k of row group (g, r16) sits in slot k ^ ((r16 >> 2) & 3) (A) or
+//   k ^ ((r16 >> 1) & 7) (B), so that the 16 rows that one read touches fall in different bank
+//   slots (see swzr).
 // The per-lane offsets are formed here, once per chunk (an empty asm keeps the compiler from
 // keeping them live across the K loop).
 template <int FA, int FB, int KS, bool PK>
@@ -163,10 +172,10 @@ __device__ __forceinline__ void mx_issue_scales(uint32_t dsa, uint32_t dsb, cons
     if constexpr (PK) {
       const int p = (wave * SC_INSTR + i) * 64 + ln;   // dword of the chunk this lane writes
       const int fa = p & 3, sa = (p >> 2) & 7, ra = (p >> 5) & 15, ga = p >> 9;
-      va = (uint32_t)(ga * 64 + fa * 16 + ra) * lp.srow + (sa ^ (ra & 7)) * 4 + col;
+      va = (uint32_t)(ga * 64 + fa * 16 + ra) * lp.srow + (sa ^ ((ra >> 2) & 3)) * 4 + col;
       const int jb = p & 7, sb = (p >> 3) & 7, rb = (p >> 6) & 15, gb = p >> 10;
       const int lr = gb * 128 + jb * 16 + rb;
-      vb = (uint32_t)((lr & 128) | b_col(lr & 127)) * lp.srow + (sb ^ (rb & 7)) * 4 + col;
+      vb = (uint32_t)((lr & 128) | b_col(lr & 127)) * lp.srow + (sb ^ ((rb >> 1) & 7)) * 4 + col;
     } else {
       const int r = wave * 32 + 8 * i + (ln >> 3), dw = ln & 7;
       va = (uint32_t)r * lp.srow + dw * 4 + col;
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
   constexpr bool PK = FA == FB;
   const int base_sa = PK ? L::SA_REGION + (wm * 16 + r16) * 128 : L::SA_REGION + (wm * WM + r16) * SC_CHUNK * 4;
   const int base_sb = PK ? L::SB_REGION + (wn * 16 + r16) * 256 : L::SB_REGION + (wn * WN + r16) * SC_CHUNK * 4;
-  const int slot_x = r16 & 7;
+  const int slot_xa = (r16 >> 2) & 3, slot_xb = (r16 >> 1) & 7;
   // v_perm selector: byte q of the low source to byte 0, byte q of the high source to byte 1
   const int sel01 = q | ((4 + q) << 8) | (0x0c << 16) | (0x0c << 24);
 
@@ -317,11 +326,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void mx_kernel(GemmArgs p, int n_block
   // 4 h + 3, in one read; pack4 keeps byte q of each (the lane's chunk), fragment f in byte f,
   // which the MFMA then selects.
   auto raw_a = [&](int g) {
-    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_x) * 16);
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_xa) * 16);
     return lds_read16(smem + base_sa + so);
   };
   auto raw_b = [&](int g, int h) {
-    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_x) * 32) + h * 16;
+    const int so = ((cbase + g / SC_CHUNK) & 1) * SC_BYTES + (((g % SC_CHUNK) ^ slot_xb) * 32) + h * 16;
     return lds_read16(smem + base_sb + so);
   };
   auto pack4 = [&](const v4i d) {
