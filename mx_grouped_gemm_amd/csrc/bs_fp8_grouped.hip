@@ -108,15 +108,19 @@ __device__ __forceinline__ void copy_bs(uint32_t dst, __amdgpu_buffer_rsrc_t r, 
 
 __device__ __forceinline__ void issue_scale_chunk(uint32_t dst, __amdgpu_buffer_rsrc_t r,
                                                   const CopyPlan& cp, int chunk, int wave) {
-  // Instruction i of wave w fills rows 32 w + 8 i + (lane >> 3); slot (lane & 7) of such a row
-  // holds column slot ^ ((4 w + i) & 7) = (slot ^ 4 (w & 1)) ^ i. The per-lane offsets are formed
-  // here from as_vrow (an empty asm keeps the compiler from hoisting all four out of the loop).
+  // Instruction i of wave w fills rows r = 32 w + 8 i + (lane >> 3); slot (lane & 7) of row r holds
+  // column slot ^ ((r >> 1) & 7) = slot ^ (lane >> 4) ^ 4 (i & 1). Read by rows alone (16 rows 32
+  // bytes apart, 4 lanes per row), the dword reads of a fragment's scales stalled the LDS on bank
+  // conflicts (30.6M conflict cycles per gate_up launch of the 32-expert step); with this slot
+  // order they take none (probed on gfx950 in isolation, and counted in the kernel). The per-lane
+  // offsets are formed here from as_vrow (an empty asm keeps the compiler from hoisting all four
+  // out of the loop).
   uint32_t v = cp.as_vrow + (uint32_t)__builtin_amdgcn_readfirstlane(chunk) * AS_CHUNK * 4;
-  uint32_t sl = (threadIdx.x & 7) ^ (4 * (wave & 1));
+  uint32_t sl = (threadIdx.x & 7) ^ ((threadIdx.x >> 4) & 3);
   asm volatile("" : "+v"(v), "+v"(sl));
 #pragma unroll
   for (int i = 0; i < AS_INSTR; i++)
-    buf2lds4(r, v + i * cp.as_row8 + ((sl ^ i) << 2), 0, lds_ptr(dst + i * 256));
+    buf2lds4(r, v + i * cp.as_row8 + ((sl ^ (4 * (i & 1))) << 2), 0, lds_ptr(dst + i * 256));
 }
 
 // This wave's LDS copy destinations: wb + region offset for A and B (a wave fills 4 KiB of each
@@ -258,9 +262,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
     base_a[h] = A_REGION + (wm * WM + r16) * BK + chunk;
     base_b[h] = B_REGION + (wn * WN + r16) * BK + chunk;
   }
-  // A scale of row wm*64 + 16 i + r16, K block kb of a chunk: slot kb ^ (2 i + (r16 >> 3))
+  // A scale of row wm*64 + 16 i + r16, K block kb of a chunk: slot kb ^ ((r16 >> 1) & 7)
   static_assert(AS_REGION % 32 == 0, "scale rows must be 32-byte aligned");
-  const int base_as = (AS_REGION + (wm * WM + r16) * AS_CHUNK * 4) | ((r16 >> 3) << 2);
+  const int base_as = (AS_REGION + (wm * WM + r16) * AS_CHUNK * 4) | (((r16 >> 1) & 7) << 2);
   const int base_bs = BS_REGION + wn * 256;
 
   CopyPlan cp;
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           ba[h] = A_REGION + (hm * WM + r16) * BK + chunk;
           bb[h] = B_REGION + ((hq >> 1) * 128 + (hq & 1) * 64 + r16) * BK + chunk;
         }
-        bas = (AS_REGION + (hm * WM + r16) * AS_CHUNK * 4) | ((r16 >> 3) << 2);
+        bas = (AS_REGION + (hm * WM + r16) * AS_CHUNK * 4) | (((r16 >> 1) & 7) << 2);
         bbs = BS_REGION + (hq >> 1) * 256;
         asm volatile("" : "+v"(ba[0]), "+v"(ba[1]), "+v"(bb[0]), "+v"(bb[1]), "+v"(bas));
       } else {
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
         bq[1] = read_frag(smem + 2048, bb);
         const int as0 = (bas ^ ((kb0 % AS_CHUNK) * 4)) + (cbase & 1) * AS_BYTES;
   #pragma unroll
-        for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + (as0 ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
+        for (int i = 0; i < MI; i++) as_raw[i] = *(const float*)(smem + as0 + i * 16 * AS_CHUNK * 4);
         bs_raw = *(const float*)(smem + bbs);
       }
 
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
           const int as_v = (bas ^ ((bn % AS_CHUNK) * 4)) + ((cbase + bn / AS_CHUNK - c0) & 1) * AS_BYTES;
   #pragma unroll
           for (int i = 0; i < MI; i++)
-            as_raw[i] = *(const float*)(smem + (as_v ^ (8 * i)) + i * 16 * AS_CHUNK * 4);
+            as_raw[i] = *(const float*)(smem + as_v + i * 16 * AS_CHUNK * 4);
           bs_raw = *(const float*)(smem + sn_bs + bbs);
         }
         __builtin_amdgcn_sched_barrier(0);
