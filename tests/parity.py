@@ -87,22 +87,18 @@ def check(prob, out, C_gpu, rows=None, tile_map_ref=None, label=""):
     return err
 
 
-# Row offsets inside each 16-row fragment band of a 128-row tile: band b takes a row from its
-# lower (0) or upper (1) half so that the eight rows fall in all eight classes of (r >> 3) & 7,
-# the row classes of the kernels' A-scale staging swizzle.
-_BAND_HALF = (0, 1, 0, 1, 1, 0, 1, 0)
-
-
 def sample_rows(prob, per_tile=12, seed=0):
     """Rows of every 128-row tile to compare: the first and the last, one row in each of the
-    tile's eight 16-row fragment bands (a random row of the half given by ``_BAND_HALF``, so the
-    eight rows cover every A-scale swizzle class), and ``per_tile - 10`` random rows."""
+    tile's eight 16-row fragment bands, and ``per_tile - 10`` random rows. Band b gives row
+    16 b + 2 b or 16 b + 2 b + 1 (at random), so that the eight rows cover all eight classes of
+    (r >> 1) & 7 (the LDS slot swizzle of the staged A scales) and of (r >> 3) & 7 (the row bits
+    above a fragment's 8-row half)."""
     rng = np.random.default_rng(seed)
     rows = []
     for t in range(0, prob.M, 128):
         hi = min(t + 128, prob.M)
         cand = [t, hi - 1]
-        cand += [t + 16 * b + 8 * h + int(rng.integers(0, 8)) for b, h in enumerate(_BAND_HALF)]
+        cand += [t + 16 * b + 2 * b + int(rng.integers(0, 2)) for b in range(8)]
         cand += [int(r) for r in rng.integers(t, hi, size=max(per_tile - 10, 0))]
         rows += [r for r in cand if r < hi]
     return np.unique(rows)
