@@ -61,7 +61,7 @@ METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 # HBM bytes per gate_up launch: rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
 # 1 GiB device copy measured with the same counters). Valid only for the kernel source whose
 # sha256 starts with this prefix; reported as null for any other source.
-GATE_UP_TRAFFIC = ("9630f28f843f73d5", 12.39e9)
+GATE_UP_TRAFFIC = ("266e8abc5f5b6400", 13.26e9)
 KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
 
 
@@ -69,9 +69,9 @@ KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_groupe
 # prefix of that source, HBM bytes per launch).
 SINGLE_TRAFFIC = {
     "nvfp4_8192": ("nv_fp4.hip", "0c838a70d41842ac", 0.590e9),
-    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "5ccf8e7a09d92b53", 1.044e9),
-    "mx8192_e4m3_e2m1": ("mx_scaled.hip", "5ccf8e7a09d92b53", 0.842e9),
-    "mx8192_e2m1_e2m1": ("mx_scaled.hip", "5ccf8e7a09d92b53", 0.572e9),
+    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "6272cc8572169feb", 1.064e9),
+    "mx8192_e4m3_e2m1": ("mx_scaled.hip", "6272cc8572169feb", 0.842e9),
+    "mx8192_e2m1_e2m1": ("mx_scaled.hip", "6272cc8572169feb", 0.572e9),
 }
 
 
