@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bw_fp8_grouped_kernel(GemmArgs p,
   // Work order: the grid is a multiple of 8 and blocks are dispatched round-robin over the 8
   // XCDs, so block b runs on XCD b % 8. In each round of G = grid items, the blocks of one XCD
   // take a contiguous run of G / 8 items; items walk groups of group_m super-tiles column block by
-  // column block, so the 32 items in flight on an XCD (8 super-tiles x 4 column blocks) share A
+  // column block, so the 32 items in flight on an XCD (4 super-tiles x 8 column blocks) share A
   // rows and B columns in its L2. (One super-tile across all its column blocks fetched a third
   // more beyond L2 and measured 3-9 % slower.)
   const int xb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
@@ -803,10 +803,12 @@ hipError_t launch_out(const GemmArgs& a, int n_blocks, unsigned grid, SplitArgs 
 template <bool SPLIT, bool LAST_RANGES = false>
 hipError_t launch(const GemmArgs& a0, int out, int n_blocks, unsigned grid, SplitArgs sp, hipStream_t stream) {
   GemmArgs a = a0;
-  // Super-tiles per group of the work order (see the kernel): 8, so that an XCD's 32 items in
-  // flight are 8 super-tiles x 4 column blocks; with at most 8 column blocks, 1 (4 super-tiles x 8
-  // column blocks), which measured 10-15 % faster on the 8-expert N = 2048 workload.
-  a.group_m = n_blocks <= 8 ? 1 : 8;
+  // Super-tiles per group of the work order (see the kernel): 4, so that an XCD's 32 items in
+  // flight are 4 super-tiles x 8 column blocks (32-expert step, alternating runs on one box:
+  // groups of 2 / 4 / 8 / 16 super-tiles 5.286 / 5.197 / 5.214 / 5.360 ms); with at most 8
+  // column blocks, 1 (4 super-tiles x 8 column blocks as well), which measured 10-15 % faster
+  // than 8 on the 8-expert N = 2048 workload.
+  a.group_m = n_blocks <= 8 ? 1 : 4;
   switch (out) {
     case kOutF32: return launch_out<kOutF32, SPLIT, LAST_RANGES>(a, n_blocks, grid, sp, stream);
     case kOutBF16: return launch_out<kOutBF16, SPLIT, LAST_RANGES>(a, n_blocks, grid, sp, stream);

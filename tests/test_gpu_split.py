@@ -71,9 +71,9 @@ def tail_parts(tiles, N, K, slots=None):
 
 def item_cell(L, tiles, N):
     """(super-tile, first column) of work item L in the kernel's order: groups of group_m
-    super-tiles (1 with at most 8 column blocks, else 8) walk their column blocks together."""
+    super-tiles (1 with at most 8 column blocks, else 4) walk their column blocks together."""
     n_blocks = -(-N // 256)
-    group_m = 1 if n_blocks <= 8 else 8
+    group_m = 1 if n_blocks <= 8 else 4
     gsz = group_m * n_blocks
     g0 = (L // gsz) * group_m
     gm = min(group_m, (tiles + 1) // 2 - g0)
