@@ -61,7 +61,7 @@ METRIC = "TFLOP/s + % of MI355X FP8 dense peak, grouped blockwise-FP8 GEMM"
 # HBM bytes per gate_up launch: rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
 # 1 GiB device copy measured with the same counters). Valid only for the kernel source whose
 # sha256 starts with this prefix; reported as null for any other source.
-GATE_UP_TRAFFIC = ("266e8abc5f5b6400", 13.26e9)
+GATE_UP_TRAFFIC = ("515145f85fe03e74", 9.89e9)
 KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_grouped.hip")
 
 
