@@ -110,12 +110,18 @@ __global__ __launch_bounds__(kRankThreads) void permute_rank_kernel(
       before += w < wave ? t : 0;
       total += t;
     }
-    int r = running + before + pre;
+    // the thread's matches in pick order, one store per match: the loop runs as many times as
+    // the most matches of a lane in the wave, not once per pick
+    if (part == 0) {
+      uint32_t mask = 0;
 #pragma unroll
-    for (int k = 0; k < kRankPer; k++) {
-      if (id[k] == e) {
+      for (int k = 0; k < kRankPer; k++) mask |= (uint32_t)(id[k] == e) << k;
+      int r = running + before + pre;
+      while (mask) {
+        const int k = __builtin_ctz(mask);
+        mask &= mask - 1;
         const long long row = off + r;
-        if (part == 0) dest[i0 + k] = row >= 0 && row < M ? (int32_t)row : -1;
+        dest[i0 + k] = row >= 0 && row < M ? (int32_t)row : -1;
         r++;
       }
     }
