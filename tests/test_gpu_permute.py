@@ -109,10 +109,12 @@ def test_moe32_full_size_sampled():
 
 
 @pytest.mark.parametrize("T,k,E,K,dtype", [(97, 10, 16, 128, torch.float32),
-                                            (64, 3, 4096, 256, torch.bfloat16)])
+                                            (64, 3, 4096, 256, torch.bfloat16),
+                                            (50, 1, 1, 256, torch.bfloat16)])
 def test_edge_shapes(T, k, E, K, dtype):
-    """top_k above 8 (the quantiser's destinations come in groups of 8), one K block, and the
-    largest expert count (a 16 KiB LDS histogram); most of the 4096 experts stay empty."""
+    """top_k above 8 (the quantiser's destinations come in groups of 8), one K block, the
+    largest expert count (a 16 KiB LDS histogram; most of the 4096 experts stay empty), and a
+    single expert (its 78 padding rows shared by the 256 workgroups that rank it)."""
     rng = np.random.default_rng(T + k)
     ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
     x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(dtype)
