@@ -304,7 +304,7 @@ def test_mx_e2m1_k_depths(K):
     check(p, "f32", C, label=f"mx e2m1xe2m1 K={K}")
 
 
-@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e4m3", "e2m1")])
+@pytest.mark.parametrize("fa,fb", MX_PAIRS)
 def test_mx_ragged_rows_and_columns(fa, fb):
     """M = 200 and N = 384: the super-tile's last 56 rows and the second column block's last 128
     columns lie past the operands, so their staged scales (packed for a pair of one format) are
@@ -399,7 +399,7 @@ def test_mx8192_sampled(name):
         f"{float(np.max(r)):.3f}, elements above the bound {float(np.mean(r > 1)):.2e}")
 
 
-@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e2m1")])
+@pytest.mark.parametrize("fa,fb", MX_PAIRS)
 def test_mx_deterministic(fa, fb):
     """Two runs of the same MX launch give the same bits."""
     p = mx_problem(1024, 768, 1024, fa, fb, device="cuda", seed=11)
