@@ -69,9 +69,9 @@ KERNEL_SOURCE = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", "bs_fp8_groupe
 # prefix of that source, HBM bytes per launch).
 SINGLE_TRAFFIC = {
     "nvfp4_8192": ("nv_fp4.hip", "0c838a70d41842ac", 0.590e9),
-    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "c555fc0a6f295bd9", 1.064e9),
-    "mx8192_e4m3_e2m1": ("mx_scaled.hip", "c555fc0a6f295bd9", 0.842e9),
-    "mx8192_e2m1_e2m1": ("mx_scaled.hip", "c555fc0a6f295bd9", 0.572e9),
+    "mx8192_e4m3_e4m3": ("mx_scaled.hip", "8de21e6fe08ece45", 1.064e9),
+    "mx8192_e4m3_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.842e9),
+    "mx8192_e2m1_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.572e9),
 }
 
 

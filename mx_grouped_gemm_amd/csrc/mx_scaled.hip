@@ -647,7 +647,7 @@ hipError_t launch_mx(const GemmArgs& a0, int fmt_a, int fmt_b, int out, hipStrea
   // persistent grid: one workgroup per compute unit (the LDS ring allows one), fewer when there
   // are fewer items; a multiple of 8 for the XCD-aware order. Work order in groups of 8
   // super-tiles, or 1 when there are at most 8 column blocks (groups of 4, as the blockwise
-  // kernel uses, measured 1 % slower for e4m3 x e4m3 and 1 % faster for e2m1 x e2m1).
+  // kernel uses, measured 1 % slower for e4m3 x e4m3 and the same for e2m1 x e2m1).
   const dim3 grid(grid_for(blocks < a0.num_cus ? blocks : a0.num_cus));
   GemmArgs a = a0;
   a.group_m = n_blocks <= 8 ? 1 : 8;
