@@ -73,6 +73,12 @@ SINGLE_TRAFFIC = {
     "mx8192_e4m3_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.842e9),
     "mx8192_e2m1_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.572e9),
 }
+# ... and of the HBM-bound launches: one bsgemm_quantize_permute call (permute_rank + quantize
+# kernels) of permute_moe32, one compact-layout small-M launch of decode_moe32.
+OTHER_TRAFFIC = {
+    "permute_moe32": ("permute.hip", "4db403de2891d156", 1.233e9),
+    "decode_moe32": ("bs_fp8_small_m.hip", "edf5075f273bfb63", 0.907e9),
+}
 
 
 def _source_matches(path, prefix):
@@ -88,6 +94,12 @@ def measured_traffic_single(workload, K):
     if workload not in SINGLE_TRAFFIC or K != 8192:
         return None
     src, prefix, nbytes = SINGLE_TRAFFIC[workload]
+    path = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", src)
+    return nbytes if _source_matches(path, prefix) else None
+
+
+def measured_traffic_other(workload):
+    src, prefix, nbytes = OTHER_TRAFFIC[workload]
     path = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", src)
     return nbytes if _source_matches(path, prefix) else None
 
@@ -364,7 +376,7 @@ def bench_permute(args, torch, bsg):
         "roofline": {
             "kernel": "permute_rank_kernel + quantize_kernel (one bsgemm_quantize_permute call)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic_other("permute_moe32"),
         },
     }
     if not args.no_cpu_baseline:
@@ -447,7 +459,7 @@ def bench_decode(args, torch, bsg):
         "roofline": {
             "kernel": "bw_fp8_small_m_kernel (gate_up, decode batch, compact layout)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic_other("decode_moe32"),
         },
     }
     if not args.no_cpu_baseline:
