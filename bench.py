@@ -73,11 +73,15 @@ SINGLE_TRAFFIC = {
     "mx8192_e4m3_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.842e9),
     "mx8192_e2m1_e2m1": ("mx_scaled.hip", "8de21e6fe08ece45", 0.572e9),
 }
-# ... and of the HBM-bound launches: one bsgemm_quantize_permute call (permute_rank + quantize
-# kernels) of permute_moe32, one compact-layout small-M launch of decode_moe32.
+# ... and of other launches: one bsgemm_quantize_permute call (permute_rank + quantize kernels)
+# of permute_moe32, one compact-layout small-M launch of decode_moe32, and one default launch
+# (bsgemm_grouped_ws, large tiles) of the smaller blockwise workloads, partial tiles included.
 OTHER_TRAFFIC = {
     "permute_moe32": ("permute.hip", "4db403de2891d156", 1.233e9),
     "decode_moe32": ("bs_fp8_small_m.hip", "edf5075f273bfb63", 0.907e9),
+    "dense_4096": ("bs_fp8_grouped.hip", "515145f85fe03e74", 0.136e9),
+    "moe8_n2048_k4096": ("bs_fp8_grouped.hip", "515145f85fe03e74", 0.325e9),
+    "dense_256x2048x16384": ("bs_fp8_grouped.hip", "515145f85fe03e74", 0.119e9),
 }
 
 
@@ -99,6 +103,8 @@ def measured_traffic_single(workload, K):
 
 
 def measured_traffic_other(workload):
+    if workload not in OTHER_TRAFFIC:
+        return None
     src, prefix, nbytes = OTHER_TRAFFIC[workload]
     path = os.path.join(ROOT, "mx_grouped_gemm_amd", "csrc", src)
     return nbytes if _source_matches(path, prefix) else None
@@ -572,7 +578,8 @@ def bench_blockwise(args, torch, bsg, make_problem):
                      "bound": "mfma",
                      "achieved": round(kernel_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": (measured_traffic_other(args.workload)
+                                 if ws is not None and not args.sched_small_m else None)},
     }
     if not args.no_cpu_baseline:
         # the oracle on about 10 s of work: dense, all 4096 rows; grouped, up to 512 real rows of
